@@ -1,0 +1,220 @@
+"""Oracle of the SVDQuant linear layer: Y ~ Q4(X diag(lam)^-1) Q4(R) + (X diag(lam)^-1 L1) L2.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__`` for the page short names cited below).
+
+Layout convention: X is [M, K] (tokens x input channels), W is [K, N], Y = X W.  Groups are 64
+consecutive input channels (k); G = K / 64.
+
+Method, as the pages describe it (SVDQ "technical principles"; FLUX4 2.2 "three steps";
+DCMP "SVDQuant" section):
+  1. smoothing moves activation outliers into the weights:  X^ = X diag(lam)^-1, W^ = diag(lam) W;
+  2. an SVD of W^ keeps the top-r singular triplets as a 16-bit low-rank branch L1 L2;
+  3. the residual R = W^ - L1 L2 is quantized to 4 bits (the Eckart-Young-Mirsky theorem says
+     removing the dominant singular values shrinks the residual's magnitude);
+  4. activations are quantized dynamically at run time (FLUX4 3.1 "dynamic activation
+     quantization"), with the symmetric rule of W4A8 3.1:
+        scale = max|v| / (2^(b-1) - 1),  q = clamp(round(v / scale), -2^(b-1), 2^(b-1) - 1);
+  5. Y = sum over groups of s_x s_w (integer dot products) + (X^ L1) L2 (+ bias).
+
+Readings where the pages are silent (each listed with its reason in the design notes):
+  * lam_k = max_m|X_mk|^alpha / max_n|W_kn|^(1-alpha) (SmoothQuant's rule; SmoothQuant is named on
+    DCMP), lam_k = 1 when either max is 0; lam is stored as fp32 and the kernels get
+    inv_lam = fl32(1 / lam32); W^ = lam32 * W in fp64.
+  * L1 = U_r diag(S_r), L2 = V_r^T, both rounded to bf16; R = W^ - L1b L2b (against the rounded
+    factors, so the 16-bit branch's rounding is absorbed by the residual), stored as fp32.
+  * b = 4, groups of 64 along k for both X (per row) and R (per output column); the scale is
+    s = fp16(fl32(amax / 7)) and codes are computed with the stored fp16 scale:
+    q = clamp(rne(fl32(v / s)), -8, 7); s = 0 gives all-zero codes.
+  * two codes per byte, even k in the low nibble, two's complement.
+  * the low-rank product T = X^ L1b and the output are evaluated in fp64 here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import decode_bf16, round_bf16, round_fp16
+
+GROUP = 64
+QMIN, QMAX = -8, 7
+
+
+# --------------------------------------------------------------------------- weight preparation
+def smoothing_factors(X: np.ndarray, W: np.ndarray, alpha: float):
+    """Per-input-channel smoothing factor (SVDQ "technical principles": smoothing migrates
+    activation outliers into the weights).
+
+    X [M, K] and W [K, N] are float64. Returns (lam32, inv_lam32), both float32 [K].
+    """
+    a = np.max(np.abs(X), axis=0) if X.shape[0] else np.zeros(X.shape[1])
+    w = np.max(np.abs(W), axis=1)
+    lam = np.ones(X.shape[1], dtype=np.float64)
+    ok = (a > 0) & (w > 0)
+    lam[ok] = a[ok] ** alpha / w[ok] ** (1.0 - alpha)
+    lam32 = lam.astype(np.float32)
+    inv32 = np.float32(1.0) / lam32
+    return lam32, inv32
+
+
+def low_rank_split(W_hat: np.ndarray, rank: int) -> dict:
+    """Truncated SVD of the smoothed weight (FLUX4 2.2, SVDQ "technical principles").
+
+    Returns the fp64 factors (L1 = U_r S_r, L2 = V_r^T), their bf16 roundings, the fp64
+    residual R = W^ - L1b L2b, R32 = fl32(R) and all singular values of W^.
+    """
+    K, N = W_hat.shape
+    U, S, Vt = np.linalg.svd(W_hat, full_matrices=False)
+    L1 = U[:, :rank] * S[None, :rank]
+    L2 = Vt[:rank, :]
+    L1b = round_bf16(L1)
+    L2b = round_bf16(L2)
+    R = W_hat - L1b @ L2b if rank > 0 else W_hat.copy()
+    return dict(L1=L1, L2=L2, L1b=L1b, L2b=L2b, R=R, R32=R.astype(np.float32), S=S)
+
+
+def prepare_weights(X_bits, W_bits, alpha: float, rank: int) -> dict:
+    """Offline preparation: smoothing factors from the calibration activations, the low-rank
+    split of the smoothed weight and the fp32 residual that gets quantized."""
+    X = decode_bf16(X_bits)
+    W = decode_bf16(W_bits)
+    lam32, inv32 = smoothing_factors(X, W, alpha)
+    W_hat = lam32.astype(np.float64)[:, None] * W
+    out = low_rank_split(W_hat, rank)
+    out.update(lam32=lam32, inv_lambda=inv32, W_hat=W_hat)
+    return out
+
+
+# --------------------------------------------------------------------------- 4-bit quantizer
+def quantize_groups(V32: np.ndarray):
+    """Symmetric INT4 quantization of each length-64 vector along the last axis
+    (W4A8 3.1 "quantization process": scale from the max magnitude over 2^(b-1)-1, round,
+    clamp to the b-bit range; here b = 4).
+
+    V32: float32 [..., 64]. Returns (codes int8 [..., 64], scales float16 [...]).
+    """
+    V32 = np.asarray(V32, dtype=np.float32)
+    assert V32.shape[-1] == GROUP
+    amax = np.max(np.abs(V32), axis=-1)
+    s16 = round_fp16(amax / np.float32(7.0))
+    if np.any(np.isinf(s16)):
+        raise ValueError("group max / 7 exceeds the fp16 range (outside the contract)")
+    s32 = s16.astype(np.float32)
+    zero = s32 == 0
+    quot = V32 / np.where(zero, np.float32(1.0), s32)[..., None]
+    q = np.clip(np.rint(quot), QMIN, QMAX).astype(np.int8)
+    q[zero] = 0
+    return q, s16
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """[rows, K] int codes in [-8, 7] -> [rows, K/2] bytes; even k in the low nibble."""
+    c = np.asarray(codes).astype(np.int16) & 0xF
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_nibbles``: [rows, K/2] bytes -> [rows, K] int8 codes."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    lo, hi = p & 0xF, p >> 4
+    out = np.empty((p.shape[0], 2 * p.shape[1]), dtype=np.int16)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return np.where(out >= 8, out - 16, out).astype(np.int8)
+
+
+def pack_weights(R32: np.ndarray) -> dict:
+    """Quantize the fp32 residual R [K, N] per (64-group of k, output column n).
+
+    Returns wq uint8 [N, K/2] (k-contiguous per column), s_w float16 [G, N], codes int8 [N, K].
+    """
+    K, N = R32.shape
+    G = K // GROUP
+    per_col = np.ascontiguousarray(np.asarray(R32, dtype=np.float32).T).reshape(N, G, GROUP)
+    q, s16 = quantize_groups(per_col)
+    codes = q.reshape(N, K)
+    return dict(wq=pack_nibbles(codes), s_w=np.ascontiguousarray(s16.T), codes=codes)
+
+
+# --------------------------------------------------------------------------- activations
+def smooth_activations(X_bits, inv_lam32: np.ndarray) -> np.ndarray:
+    """X^ = fl32(fl32(X) * inv_lam): the smoothing divide as one fp32 multiply by the stored
+    reciprocal."""
+    X32 = decode_bf16(X_bits).astype(np.float32)
+    return X32 * np.asarray(inv_lam32, dtype=np.float32)[None, :]
+
+
+def quantize_act(X_bits, inv_lam32, L1b) -> dict:
+    """Dynamic INT4 activation quantization per (token, 64-group) and the low-rank
+    down-projection T = X^ L1b (fp64 of the fp32 X^)."""
+    Xh = smooth_activations(X_bits, inv_lam32)
+    M, K = Xh.shape
+    G = K // GROUP
+    q, s16 = quantize_groups(Xh.reshape(M, G, GROUP))
+    codes = q.reshape(M, K)
+    T = None
+    if L1b is not None and np.asarray(L1b).shape[1] > 0:
+        T = Xh.astype(np.float64) @ np.asarray(L1b, dtype=np.float64)
+    return dict(xq=pack_nibbles(codes), s_x=s16, codes=codes, X_hat=Xh, T=T)
+
+
+# --------------------------------------------------------------------------- integer GEMM
+def int_partials(cx: np.ndarray, cw: np.ndarray) -> np.ndarray:
+    """P[g, m, n] = sum_{k in group g} cx[m, k] cw[n, k] (cx [M, K], cw [N, K] int codes).
+
+    Evaluated with fp64 matrix products on integer-valued matrices: every product and partial
+    sum is an integer of magnitude <= 64 * 64, far below 2^53, so the result is exact.
+    """
+    M, K = cx.shape
+    N = cw.shape[0]
+    G = K // GROUP
+    P = np.empty((G, M, N), dtype=np.int32)
+    for g in range(G):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        P[g] = np.rint(cx[:, sl].astype(np.float64) @ cw[:, sl].astype(np.float64).T)
+    return P
+
+
+def int_partials_bruteforce(cx, cw):
+    """Pure-Python triple loop of ``int_partials`` for tiny shapes."""
+    M, K = len(cx), len(cx[0])
+    N = len(cw)
+    G = K // GROUP
+    P = np.zeros((G, M, N), dtype=np.int64)
+    for g in range(G):
+        for m in range(M):
+            for n in range(N):
+                acc = 0
+                for k in range(g * GROUP, (g + 1) * GROUP):
+                    acc += int(cx[m][k]) * int(cw[n][k])
+                P[g, m, n] = acc
+    return P
+
+
+def linear_output(cx, s_x, cw, s_w, T=None, L2b=None, bias_bits=None) -> np.ndarray:
+    """Y[m, n] = sum_g s_x[m, g] s_w[g, n] P[g, m, n] + (T L2b)[m, n] + bias[n]   (fp64).
+
+    The low-rank term is the 16-bit branch kept beside the 4-bit product (SVDQ "technical
+    principles"); the bias is optional.
+    """
+    M, K = cx.shape
+    N = cw.shape[0]
+    G = K // GROUP
+    Y = np.zeros((M, N), dtype=np.float64)
+    sx = np.asarray(s_x, dtype=np.float64)
+    sw = np.asarray(s_w, dtype=np.float64)
+    for g in range(G):
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        Pg = cx[:, sl].astype(np.float64) @ cw[:, sl].astype(np.float64).T
+        Y += (sx[:, g:g + 1] * sw[g:g + 1, :]) * Pg
+    if T is not None and L2b is not None and np.asarray(L2b).shape[0] > 0:
+        Y += np.asarray(T, dtype=np.float64) @ np.asarray(L2b, dtype=np.float64)
+    if bias_bits is not None:
+        Y += decode_bf16(bias_bits)[None, :]
+    return Y
+
+
+def svdq_linear(X_bits, inv_lam32, L1b, L2b, packed_w: dict, bias_bits=None) -> dict:
+    """Whole forward pass of one SVDQuant linear given prepared weights."""
+    act = quantize_act(X_bits, inv_lam32, L1b)
+    Y = linear_output(act["codes"], act["s_x"], packed_w["codes"], packed_w["s_w"],
+                      act["T"], L2b, bias_bits)
+    act["Y"] = Y
+    return act
