@@ -1,0 +1,182 @@
+// C ABI of libsvdq (declared in include/svdq.h): argument validation and kernel dispatch.
+//
+// Every entry point checks all of its arguments before touching the HIP runtime, so a
+// rejected call has no side effect at all (no launch, no device state, outputs untouched).
+#include "svdq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "svdq_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = {0};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = 0;
+  return SVDQ_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SVDQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr long long kMaxElems = 1LL << 40;  // keeps every byte offset far inside size_t
+constexpr int kMaxRank = 128;
+
+int check_k(int K) {
+  if (K <= 0) return fail(SVDQ_EINVAL, "K must be positive (got %d)", K);
+  if (K % 64 != 0) return fail(SVDQ_ESHAPE, "K must be a multiple of 64 (got %d)", K);
+  return SVDQ_OK;
+}
+
+int check_rank(int r) {
+  if (r < 0) return fail(SVDQ_EINVAL, "r must be >= 0 (got %d)", r);
+  if (r % 16 != 0 || r > kMaxRank)
+    return fail(SVDQ_ESHAPE, "r must be a multiple of 16 in [0, %d] (got %d)", kMaxRank, r);
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+const char* svdq_status_str(int status) {
+  switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_EINVAL: return "invalid argument";
+    case SVDQ_ESHAPE: return "unsupported shape";
+    case SVDQ_EALIGN: return "misaligned pointer";
+    case SVDQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* svdq_last_error(void) { return g_last_error; }
+
+int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
+                      void* stream) {
+  if (int s = check_k(K)) return s;
+  if (N <= 0) return fail(SVDQ_EINVAL, "N must be positive (got %d)", N);
+  if ((long long)K * N > kMaxElems) return fail(SVDQ_ESHAPE, "K * N too large");
+  if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535");
+  if (!R || !wq || !w_scales) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(R) || !aligned16(wq)) return fail(SVDQ_EALIGN, "R and wq must be 16-byte aligned");
+  return hip_status(svdq::launch_pack_weights(R, K, N, wq, w_scales, (hipStream_t)stream),
+                    "svdq_pack_weights");
+}
+
+int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                      int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream) {
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0 (got %d)", M);
+  if (int s = check_k(K)) return s;
+  if (int s = check_rank(r)) return s;
+  if ((long long)M * K > kMaxElems) return fail(SVDQ_ESHAPE, "M * K too large");
+  if (!X || !inv_lambda || !xq || !x_scales) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (r > 0 && (!L1 || !T)) return fail(SVDQ_EINVAL, "L1 and T are required when r > 0");
+  if (!aligned16(X) || !aligned16(inv_lambda) || !aligned16(xq) || (r > 0 && !aligned16(L1)))
+    return fail(SVDQ_EALIGN, "X, inv_lambda, xq and L1 must be 16-byte aligned");
+  if (M == 0) return ok();
+  return hip_status(svdq::launch_quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T,
+                                              (hipStream_t)stream),
+                    "svdq_quantize_act");
+}
+
+static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K) {
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0 (got %d)", M);
+  if (N <= 0) return fail(SVDQ_EINVAL, "N must be positive (got %d)", N);
+  if (int s = check_k(K)) return s;
+  if ((long long)M * N > kMaxElems || (long long)M * K > kMaxElems || (long long)N * K > kMaxElems)
+    return fail(SVDQ_ESHAPE, "problem too large");
+  if ((M + 127) / 128 > 65535) return fail(SVDQ_ESHAPE, "M too large for one launch");
+  if (!xq || !wq) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(xq) || !aligned16(wq)) return fail(SVDQ_EALIGN, "xq and wq must be 16-byte aligned");
+  return SVDQ_OK;
+}
+
+int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
+                   void* stream) {
+  if (int s = check_gemm(xq, wq, M, N, K)) return s;
+  if (int s = check_rank(r)) return s;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_FP32)
+    return fail(SVDQ_EINVAL, "out_dtype must be SVDQ_OUT_BF16 or SVDQ_OUT_FP32");
+  if (!x_scales || !w_scales || !Y) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (r > 0 && (!T || !L2)) return fail(SVDQ_EINVAL, "T and L2 are required when r > 0");
+  if (!aligned16(Y) || (r > 0 && (!aligned16(T) || !aligned16(L2))))
+    return fail(SVDQ_EALIGN, "Y, T and L2 must be 16-byte aligned");
+  if (M == 0) return ok();
+  return hip_status(svdq::launch_w4a4_gemm(xq, x_scales, T, wq, w_scales, L2, bias, M, N, K, r,
+                                           Y, out_dtype == SVDQ_OUT_FP32, nullptr,
+                                           (hipStream_t)stream),
+                    "svdq_w4a4_gemm");
+}
+
+int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int32_t* P,
+                       void* stream) {
+  if (int s = check_gemm(xq, wq, M, N, K)) return s;
+  if (!P) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (M == 0) return ok();
+  return hip_status(svdq::launch_w4a4_gemm(xq, nullptr, nullptr, wq, nullptr, nullptr, nullptr,
+                                           M, N, K, 0, nullptr, 0, P, (hipStream_t)stream),
+                    "svdq_w4a4_partials");
+}
+
+size_t kv_int8_workspace_bytes(int tokens, int channels) {
+  return svdq::kv_workspace_bytes(tokens, channels);
+}
+
+static int check_kv(int tokens, int channels) {
+  if (tokens < 0) return fail(SVDQ_EINVAL, "tokens must be >= 0 (got %d)", tokens);
+  if (channels <= 0) return fail(SVDQ_EINVAL, "channels must be positive (got %d)", channels);
+  if (channels % 8 != 0) return fail(SVDQ_ESHAPE, "channels must be a multiple of 8 (got %d)", channels);
+  if ((long long)tokens * channels > kMaxElems) return fail(SVDQ_ESHAPE, "tensor too large");
+  if ((tokens + 63) / 64 > 65535) return fail(SVDQ_ESHAPE, "too many tokens for one launch");
+  return SVDQ_OK;
+}
+
+int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float* scale,
+                  uint8_t* zero, void* workspace, void* stream) {
+  if (int s = check_kv(tokens, channels)) return s;
+  if (!x || !q || !scale || !zero || (tokens > 0 && !workspace))
+    return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale) || !aligned16(zero) ||
+      !aligned16(workspace))
+    return fail(SVDQ_EALIGN, "x, q, scale, zero and workspace must be 16-byte aligned");
+  if (tokens == 0) return ok();
+  return hip_status(svdq::launch_kv_quant(x, tokens, channels, q, scale, zero, workspace,
+                                          (hipStream_t)stream),
+                    "kv_int8_quant");
+}
+
+int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
+                    int channels, uint16_t* x_out, void* stream) {
+  if (int s = check_kv(tokens, channels)) return s;
+  if (!q || !scale || !zero || !x_out) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(q) || !aligned16(scale) || !aligned16(zero) || !aligned16(x_out))
+    return fail(SVDQ_EALIGN, "q, scale, zero and x_out must be 16-byte aligned");
+  if (tokens == 0) return ok();
+  return hip_status(svdq::launch_kv_dequant(q, scale, zero, tokens, channels, x_out,
+                                            (hipStream_t)stream),
+                    "kv_int8_dequant");
+}
+
+}  // extern "C"

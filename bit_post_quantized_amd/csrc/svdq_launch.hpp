@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels (one per kernel file).  Arguments are validated by
+// the C ABI layer before any of these is called; each returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace svdq {
+
+hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
+                               hipStream_t stream);
+
+hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                               int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
+                               hipStream_t stream);
+
+hipError_t launch_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                            const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                            const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                            int out_fp32, int32_t* partials, hipStream_t stream);
+
+size_t kv_workspace_bytes(int tokens, int channels);
+
+hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t* q,
+                           float* scale, uint8_t* zero, void* workspace, hipStream_t stream);
+
+hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,
+                             int tokens, int channels, uint16_t* x_out, hipStream_t stream);
+
+}  // namespace svdq

@@ -1,0 +1,96 @@
+"""SVDQuant linear layer on top of the C ABI: offline weight conversion and the forward pass.
+
+Weight conversion (offline, host): the three steps of SVDQuant (SVDQ "technical principles";
+FLUX4 2.2) — smoothing factors from calibration activations, a rank-r SVD of the smoothed
+weight kept as a bf16 low-rank branch, and the fp32 residual, which ``svdq_pack_weights``
+quantizes to packed INT4 on the device.  The SVD is a LAPACK call through torch on the host:
+it is the offline preparation a toolbox performs once per checkpoint, not part of the
+per-token path.
+
+Forward (device): ``svdq_quantize_act`` then ``svdq_w4a4_gemm``, two launches on one stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding
+
+
+@dataclass
+class PackedWeights:
+    K: int
+    N: int
+    rank: int
+    inv_lambda: torch.Tensor  # fp32 [K]
+    L1t: torch.Tensor         # bf16 [r, K]  (the [K, r] factor stored K-contiguous)
+    L2t: torch.Tensor         # bf16 [N, r]  (the [r, N] factor stored r-contiguous)
+    wq: torch.Tensor          # uint8 [N, K/2]
+    w_scales: torch.Tensor    # fp16 [K/64, N]
+    bias: Optional[torch.Tensor] = None  # bf16 [N]
+
+
+def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
+                    bias: Optional[torch.Tensor] = None, device="cuda") -> PackedWeights:
+    """W bf16 [K, N] (Y = X W), X_calib bf16 [M, K] calibration activations."""
+    K, N = W.shape
+    Wd = W.detach().to("cpu", torch.float64)
+    Xd = X_calib.detach().to("cpu", torch.float64)
+    a = Xd.abs().amax(dim=0) if Xd.shape[0] else torch.zeros(K, dtype=torch.float64)
+    w = Wd.abs().amax(dim=1)
+    ok = (a > 0) & (w > 0)
+    lam = torch.ones(K, dtype=torch.float64)
+    lam[ok] = a[ok].pow(alpha) / w[ok].pow(1.0 - alpha)
+    lam32 = lam.to(torch.float32)
+    inv32 = torch.ones(K, dtype=torch.float32) / lam32
+    W_hat = lam32.to(torch.float64)[:, None] * Wd
+    if rank > 0:
+        U, S, Vh = torch.linalg.svd(W_hat, full_matrices=False)
+        L1b = (U[:, :rank] * S[:rank]).to(torch.float32).to(torch.bfloat16)
+        L2b = Vh[:rank, :].to(torch.float32).to(torch.bfloat16)
+        R = W_hat - L1b.to(torch.float64) @ L2b.to(torch.float64)
+    else:
+        L1b = torch.zeros(K, 0, dtype=torch.bfloat16)
+        L2b = torch.zeros(0, N, dtype=torch.bfloat16)
+        R = W_hat
+    R32 = R.to(torch.float32).to(device).contiguous()
+    wq = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
+    w_scales = torch.empty(K // 64, N, dtype=torch.float16, device=device)
+    binding.svdq_pack_weights(R32, wq, w_scales)
+    return PackedWeights(
+        K=K, N=N, rank=rank, inv_lambda=inv32.to(device),
+        L1t=L1b.t().contiguous().to(device), L2t=L2b.t().contiguous().to(device),
+        wq=wq, w_scales=w_scales,
+        bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous())
+
+
+@dataclass
+class ActBuffers:
+    xq: torch.Tensor
+    x_scales: torch.Tensor
+    T: Optional[torch.Tensor]
+
+
+def alloc_act(M: int, K: int, rank: int, device="cuda") -> ActBuffers:
+    return ActBuffers(
+        xq=torch.empty(M, K // 2, dtype=torch.uint8, device=device),
+        x_scales=torch.empty(K // 64, M, dtype=torch.float16, device=device),
+        T=torch.empty(M, rank, dtype=torch.float32, device=device) if rank > 0 else None)
+
+
+def forward(X: torch.Tensor, pw: PackedWeights, out: Optional[torch.Tensor] = None,
+            act: Optional[ActBuffers] = None, out_dtype=torch.bfloat16,
+            stream=None) -> torch.Tensor:
+    """Y = SVDQuant-linear(X) for X bf16 [M, K] on the device."""
+    M, K = X.shape
+    if act is None:
+        act = alloc_act(M, K, pw.rank, X.device)
+    if out is None:
+        out = torch.empty(M, pw.N, dtype=out_dtype, device=X.device)
+    binding.svdq_quantize_act(X, pw.inv_lambda, pw.L1t if pw.rank else None, pw.rank,
+                              act.xq, act.x_scales, act.T, stream)
+    binding.svdq_w4a4_gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales,
+                           pw.L2t if pw.rank else None, pw.bias, pw.rank, out, stream)
+    return out

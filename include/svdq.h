@@ -1,0 +1,154 @@
+/*
+ * svdq.h — C ABI of the MI355X (gfx950) SVDQuant W4A4 + low-rank linear layer and the INT8
+ * KV-cache quantizer.
+ *
+ * Sources (web pages), cited below by short name:
+ *   SVDQ  "SVDQuant是什么？一文让你看懂SVDQuant的技术原理、主要功能、应用场景" (zhuoshang.net)
+ *   FLUX4 "AI图像生成4-bit量化技术解析与应用" (intelliparadigm.com)
+ *   W4A8  "W4A8量化技术在边缘计算中的实践与优化" (mhpn.cn)
+ *   VARC  "VAR-Compressor：在边缘GPU上实现80亿参数视觉自回归模型的高效量化部署" (zingnex.cn)
+ *   DCMP  "DeepCompressor：MIT 团队开源的大模型与 Diffusion 模型压缩工具箱" (pomoai.com)
+ *
+ * The layer computes  Y = Q4(X diag(lam)^-1) Q4(R) + (X diag(lam)^-1 L1) L2 + bias  where the
+ * weight W [K, N] was smoothed (W^ = diag(lam) W), split by a rank-r SVD into a 16-bit branch
+ * L1 [K, r] L2 [r, N] and a residual R = W^ - L1 L2 that is quantized to 4 bits
+ * (SVDQ "technical principles"; FLUX4 2.2).  G = K / 64 quantization groups along K.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees or keeps them, holds no global state and is safe to call from several threads.
+ *   - Arrays are dense and row-major in the layout written next to each argument; fp16 and
+ *     bf16 values are passed as their uint16 bit patterns.
+ *   - Pointers marked "16B" must be 16-byte aligned.
+ *   - Every call validates its arguments synchronously and, on error, returns a nonzero status
+ *     and launches nothing (outputs untouched).  On success the work is enqueued on `stream`
+ *     (a hipStream_t passed as void*, NULL = the default stream) and the call returns at once;
+ *     faults inside a kernel surface at the caller's next synchronization.
+ *   - Sizes of 0 rows (M = 0, tokens = 0) are valid and enqueue nothing.
+ *   - Inputs that are NaN or Inf, or whose group max / 7 exceeds the fp16 range (65504), are
+ *     outside the contract: the call succeeds but the codes and scales are unspecified.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+
+enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_EINVAL = 1, /* NULL pointer, negative or zero size where one is required */
+  SVDQ_ESHAPE = 2, /* K % 64 != 0, r % 16 != 0 or r > 128, channels % 8 != 0, too large */
+  SVDQ_EALIGN = 3, /* a "16B" pointer is not 16-byte aligned */
+  SVDQ_EHIP = 4    /* the HIP runtime refused the launch (see svdq_last_error) */
+};
+
+enum svdq_out_dtype { SVDQ_OUT_BF16 = 0, SVDQ_OUT_FP32 = 1 };
+
+/* SVDQ_ABI_VERSION of the built library. */
+int svdq_abi_version(void);
+
+/* Static text for a status code. */
+const char* svdq_status_str(int status);
+
+/* Text of the last error raised on the calling thread (empty if none). */
+const char* svdq_last_error(void);
+
+/*
+ * svdq_pack_weights — quantize the fp32 residual R to symmetric INT4 per (64-group of k,
+ * output column n) and pack two codes per byte (residual quantization: FLUX4 2.2; scale rule
+ * W4A8 3.1 with b = 4).  For each (g, n):
+ *     s = fp16(fl32(amax / 7)),  q = clamp(rne(fl32(R / s)), -8, 7),  q = 0 when s == 0.
+ *   R         fp32 [K, N]                       16B
+ *   wq        uint8 [N, K/2]; byte j of row n holds k = 2j (low nibble) and 2j+1 (high)  16B
+ *   w_scales  fp16 [G, N]
+ *   K % 64 == 0, K >= 64, N >= 1.  Offline (weight preparation), not on the timed path.
+ */
+int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
+                      void* stream);
+
+/*
+ * svdq_quantize_act — one HBM pass over the activations: smoothing divide (a multiply by the
+ * stored reciprocal inv_lambda), dynamic symmetric INT4 quantization per (token, 64-group)
+ * (FLUX4 3.1 "dynamic activation quantization"; W4A8 3.1), and the low-rank down-projection
+ * T = bf16(X^) L1 with fp32 accumulation (SVDQ "technical principles": 16-bit branch).
+ *     X^ = fl32(X * inv_lambda);  s = fp16(fl32(amax / 7));  q = clamp(rne(fl32(X^ / s)), -8, 7)
+ *   X           bf16 [M, K]                               16B
+ *   inv_lambda  fp32 [K]                                  16B
+ *   L1          bf16, the [K, r] factor stored K-contiguous: element (k, j) at L1[j*K + k]
+ *               (16B); may be NULL when r == 0
+ *   xq          uint8 [M, K/2], nibble order as wq        16B
+ *   x_scales    fp16 [G, M]  (group-major: the scales of one group are contiguous over tokens)
+ *   T           fp32 [M, r]; may be NULL when r == 0
+ *   M >= 0, K % 64 == 0, K >= 64, 0 <= r <= 128, r % 16 == 0.
+ */
+int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                      int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream);
+
+/*
+ * svdq_w4a4_gemm — the W4A4 group GEMM with the low-rank branch and bias fused into its
+ * epilogue (SVDQ "Nunchaku" kernel fusion; DCMP "SVDQuant" section):
+ *     Y[m, n] = sum_g s_x[g, m] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
+ *     P[g, m, n] = sum_{k in group g} qx[m, k] qw[n, k]   (exact int32).
+ *   xq, x_scales, T   as written by svdq_quantize_act (T: 16B; may be NULL when r == 0)
+ *   wq, w_scales      as written by svdq_pack_weights
+ *   L2          bf16, the [r, N] factor stored r-contiguous: element (j, n) at L2[n*r + j]
+ *               (16B); may be NULL when r == 0
+ *   bias        bf16 [N] or NULL
+ *   Y           [M, N], bf16 (out_dtype = SVDQ_OUT_BF16, round to nearest even) or fp32
+ *               (SVDQ_OUT_FP32)                           16B
+ *   M >= 0, N >= 1, K % 64 == 0, K >= 64, 0 <= r <= 128, r % 16 == 0.
+ */
+int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
+                   void* stream);
+
+/*
+ * svdq_w4a4_partials — test entry: the exact int32 group partials of the same device inner
+ * loop as svdq_w4a4_gemm, P[g][m][n] = sum_{k in group g} qx[m, k] qw[n, k].
+ *   P  int32 [G, M, N]
+ */
+int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int32_t* P,
+                       void* stream);
+
+/*
+ * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its
+ * cross-token min/max reduction (0 when tokens == 0).
+ */
+size_t kv_int8_workspace_bytes(int tokens, int channels);
+
+/*
+ * kv_int8_quant — asymmetric per-channel INT8 quantization of a KV-cache tensor viewed as
+ * x [tokens, channels] (channel = one (head, dim) pair; statistics over every token of the
+ * call), VARC "INT8 KV cache quantization":
+ *     lo = min(0, min_t x), hi = max(0, max_t x), s = fl32(fl32(hi - lo) / 255) (1 if 0),
+ *     z = clamp(rne(fl32(-lo / s)), 0, 255),  q = clamp(rne(fl32(x / s)) + z, 0, 255).
+ *   x          bf16 [tokens, channels]                    16B
+ *   q          uint8 [tokens, channels]                   16B
+ *   scale      fp32 [channels]    16B;   zero  uint8 [channels]    16B
+ *   workspace  device scratch of kv_int8_workspace_bytes(tokens, channels) bytes    16B
+ *   tokens >= 0, channels >= 8, channels % 8 == 0.
+ */
+int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float* scale,
+                  uint8_t* zero, void* workspace, void* stream);
+
+/*
+ * kv_int8_dequant — x' = bf16(fl32((q - z) * s)) per element (round to nearest even).
+ *   q      uint8 [tokens, channels]   16B;   x_out  bf16 [tokens, channels]   16B
+ *   scale, zero as written by kv_int8_quant   16B
+ *   tokens >= 0, channels >= 8, channels % 8 == 0.
+ */
+int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
+                    int channels, uint16_t* x_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

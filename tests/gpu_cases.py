@@ -1,0 +1,78 @@
+"""Shared inputs for the GPU parity tests: seeded workloads, the oracle's prepared weights and
+device copies in the layouts of include/svdq.h.  (Not a test module.)"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+from oracle import kv_int8 as okv
+from oracle import svdquant as osq
+from oracle.numerics import bf16_to_bits
+from synthetic import LINEAR_CONFIGS, make_kv, make_linear
+
+# (config id, M, K, N): small cases that span several 128x128 tiles with ragged tails, and the
+# full workload shapes (which run in the same launch configuration as the benchmark)
+SMALL = {
+    "c1": (1, None, None, None),
+    "c2s": (2, 300, 512, 384),
+    "c3s": (3, 257, 1024, 640),
+    "c4s": (4, 130, 2048, 200),
+}
+FULL = {"c2": (2, None, None, None), "c3": (3, None, None, None), "c4": (4, None, None, None)}
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t if dtype is None else t.to(dtype)).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=None)
+def linear_case(cid: int, M, K, N, bias: bool = False):
+    """Workload + the oracle's weight preparation and packed weights (cached per session)."""
+    d = make_linear(cid, M=M, K=K, N=N, with_bias=bias)
+    cfg = LINEAR_CONFIGS[cid]
+    pw = osq.prepare_weights(d["X"], d["W"], cfg.alpha, cfg.rank)
+    packed = osq.pack_weights(pw["R32"])
+    return d, pw, packed, cfg.rank
+
+
+def oracle_act(case):
+    d, pw, _, _ = case
+    return osq.quantize_act(d["X"], pw["inv_lambda"], pw["L1b"])
+
+
+def device_weights(case):
+    """Oracle-prepared weights in the C-ABI layouts on the device."""
+    d, pw, packed, r = case
+    return dict(
+        inv_lambda=dev(pw["inv_lambda"]),
+        L1t=dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None,
+        L2t=dev_bf16(bf16_to_bits(pw["L2b"].T)) if r else None,
+        R32=dev(pw["R32"]),
+        bias=dev_bf16(d["bias"]) if d["bias"] is not None else None,
+    )
+
+
+def max_abs_rel(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref|: the output tolerance metric (normwise)."""
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+@functools.lru_cache(maxsize=None)
+def kv_case(tokens=None, heads=None, dim=None, seed=0):
+    d = make_kv(seed=seed, tokens=tokens, heads=heads, dim=dim)
+    out = {}
+    for name in ("K", "V"):
+        x = d[name].reshape(d[name].shape[0], -1)
+        out[name] = (x, okv.kv_int8_quant(x))
+    return out

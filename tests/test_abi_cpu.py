@@ -1,0 +1,102 @@
+"""The C-ABI library loads without a GPU, exports every function include/svdq.h declares, and
+rejects invalid arguments with the documented status before touching the HIP runtime."""
+import os
+import re
+
+import pytest
+
+from bit_post_quantized_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libsvdq.so is not built (run python -m bit_post_quantized_amd.build)")
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) == 10, names
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.svdq_abi_version() == 1
+    assert lib.svdq_status_str(0) == b"ok"
+    assert lib.svdq_status_str(2) == b"unsupported shape"
+    assert lib.svdq_status_str(99) == b"unknown status"
+
+
+# a fake, 16-byte aligned, never dereferenced address: every call below must fail validation
+FAKE = 0x10000
+ODD = 0x10008
+
+
+def test_pack_weights_validation(lib):
+    assert lib.svdq_pack_weights(FAKE, 100, 8, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert lib.svdq_pack_weights(FAKE, 0, 8, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert lib.svdq_pack_weights(FAKE, 64, 0, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert lib.svdq_pack_weights(None, 64, 8, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert lib.svdq_pack_weights(ODD, 64, 8, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    lib.svdq_pack_weights(FAKE, 100, 8, FAKE, FAKE, None)
+    assert b"multiple of 64" in lib.svdq_last_error()
+
+
+def test_quantize_act_validation(lib):
+    f = lib.svdq_quantize_act
+    assert f(FAKE, FAKE, FAKE, 4, 128, 20, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 128, 144, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 96, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, -1, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, FAKE, None, 4, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, FAKE, FAKE, 4, 128, 16, FAKE, FAKE, None, None) == binding.SVDQ_EINVAL
+    assert f(ODD, FAKE, FAKE, 4, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    # M = 0 is valid and enqueues nothing (no HIP call is made)
+    assert f(FAKE, FAKE, FAKE, 0, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_OK
+
+
+def test_gemm_validation(lib):
+    g = lib.svdq_w4a4_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert g(*args, 8, 8, 100, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert g(*args, 8, 0, 128, 0, FAKE, 0, None) == binding.SVDQ_EINVAL
+    assert g(*args, 8, 8, 128, 0, FAKE, 7, None) == binding.SVDQ_EINVAL  # bad out_dtype
+    assert g(*args, 8, 8, 128, 24, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 8, 8, 128, 16, FAKE, 0, None) == binding.SVDQ_EINVAL
+    assert g(*args, 8, 8, 128, 0, ODD, 0, None) == binding.SVDQ_EALIGN
+    assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK
+    p = lib.svdq_w4a4_partials
+    assert p(FAKE, FAKE, 8, 8, 96, FAKE, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
+
+
+def test_kv_validation(lib):
+    q = lib.kv_int8_quant
+    assert lib.kv_int8_workspace_bytes(0, 4096) == 0
+    assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 160 * 4096 * 4
+    assert q(FAKE, 16, 12, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert q(FAKE, -1, 16, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert q(FAKE, 16, 16, FAKE, FAKE, FAKE, None, None) == binding.SVDQ_EINVAL
+    assert q(FAKE, 16, 16, FAKE, ODD, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    assert q(FAKE, 0, 16, FAKE, FAKE, FAKE, None, None) == binding.SVDQ_OK
+    d = lib.kv_int8_dequant
+    assert d(FAKE, FAKE, FAKE, 16, 0, FAKE, None) == binding.SVDQ_EINVAL
+    assert d(FAKE, FAKE, FAKE, 16, 16, ODD, None) == binding.SVDQ_EALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        binding.load(str(tmp_path / "missing.so"))
