@@ -45,15 +45,16 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
   for (int strip = wave; strip < nstrips; strip += nwaves) {
     const int g = strip * 4 + q;
     const bool valid = g < G;
-    const int k0 = g * kGroup;
+    const int k0 = (valid ? g : G - 1) * kGroup;  // loads stay in bounds; invalid lanes zeroed
     float xh[kGroup];
-    if (valid) {
+    {
       const v4u* xs = reinterpret_cast<const v4u*>(X + (size_t)row_ld * K + k0);
       const v4f* ls = reinterpret_cast<const v4f*>(inv_lambda + k0);
+      const float keep = valid ? 1.0f : 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const v4u w = xs[c];
-        const v4f l0 = ls[2 * c], l1 = ls[2 * c + 1];
+        const v4f l0 = ls[2 * c] * keep, l1 = ls[2 * c + 1] * keep;
         xh[8 * c + 0] = __uint_as_float(w.x << 16) * l0.x;
         xh[8 * c + 1] = __uint_as_float(w.x & 0xFFFF0000u) * l0.y;
         xh[8 * c + 2] = __uint_as_float(w.y << 16) * l0.z;
@@ -63,9 +64,6 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
         xh[8 * c + 6] = __uint_as_float(w.w << 16) * l1.z;
         xh[8 * c + 7] = __uint_as_float(w.w & 0xFFFF0000u) * l1.w;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) xh[i] = 0.0f;
     }
 
     // ---- INT4 quantization of this lane's group
@@ -75,19 +73,7 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
     const uint16_t sb = int4_scale_bits(amax);
     const float s = half_bits_to_float(sb);
     uint32_t packed[8];
-    if (s == 0.0f) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j] = 0u;
-    } else {
-      const float rcp = 1.0f / s;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w |= ((uint32_t)int4_code(xh[8 * j + e], s, rcp) & 0xFu) << (4 * e);
-        packed[j] = w;
-      }
-    }
+    quantize_group_int4(xh, s, packed);
     if (valid && row < M) {
       v4u* dst = reinterpret_cast<v4u*>(xq + (size_t)row * (K / 2) + (size_t)g * (kGroup / 2));
       dst[0] = v4u{packed[0], packed[1], packed[2], packed[3]};
@@ -107,8 +93,7 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
         const v8bf av = __builtin_bit_cast(v8bf, a);
 #pragma unroll
         for (int t = 0; t < NTR; ++t) {
-          v4u b = v4u{0u, 0u, 0u, 0u};
-          if (valid) b = *reinterpret_cast<const v4u*>(L1 + (size_t)(t * 16 + rl) * K + k0 + 8 * j);
+          const v4u b = *reinterpret_cast<const v4u*>(L1 + (size_t)(t * 16 + rl) * K + k0 + 8 * j);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, b), acc[t], 0, 0, 0);
         }
       }

@@ -27,19 +27,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
   const uint16_t sb = int4_scale_bits(amax);
   const float s = half_bits_to_float(sb);
   uint32_t packed[8];
-  if (s == 0.0f) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) packed[j] = 0u;
-  } else {
-    const float rcp = 1.0f / s;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t w = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w |= ((uint32_t)int4_code(v[8 * j + e], s, rcp) & 0xFu) << (4 * e);
-      packed[j] = w;
-    }
-  }
+  quantize_group_int4(v, s, packed);
   v4u* dst = reinterpret_cast<v4u*>(wq + (size_t)n * (K / 2) + (size_t)g * (kGroup / 2));
   dst[0] = v4u{packed[0], packed[1], packed[2], packed[3]};
   dst[1] = v4u{packed[4], packed[5], packed[6], packed[7]};

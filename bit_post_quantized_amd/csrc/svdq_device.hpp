@@ -47,18 +47,20 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- exact quantizer rounding
-// rne(fl32(x / s)) for s != 0, given rcp = fl32(1 / s).  The product t = fl32(x * rcp) lies
-// within |x/s| * 2^-22.4 of fl32(x / s); the two can only round to different integers when t
-// is that close to a half-integer, so within a (much wider) window of 2^-20 * max(1, |t|)
-// around a half-integer the quotient is recomputed with the IEEE division.
+// fl32(x / s), correctly rounded, without a division per element: with rcp = fl32(1 / s),
+// q0 = fl32(x * rcp) is within one ulp of x / s, the residual x - q0 * s is exact in one FMA,
+// and one more FMA rounds q0 + residual * rcp to the correctly rounded quotient (Markstein's
+// correction step for division with an accurate reciprocal; valid away from underflow, which
+// the codes never reach: a quotient below 2^-100 rounds to code 0 either way).
+__device__ __forceinline__ float div_rn(float x, float s, float rcp) {
+  const float q0 = x * rcp;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(r, rcp, q0);
+}
+
+// rne(fl32(x / s)) for s != 0, given rcp = fl32(1 / s).
 __device__ __forceinline__ float rne_quotient(float x, float s, float rcp) {
-  float t = x * rcp;
-  float r = __builtin_rintf(t);
-  float d = __builtin_fabsf(t - r);
-  if (__builtin_fabsf(d - 0.5f) <= 0x1p-20f * __builtin_fmaxf(1.0f, __builtin_fabsf(t))) {
-    r = __builtin_rintf(x / s);
-  }
-  return r;
+  return __builtin_rintf(div_rn(x, s, rcp));
 }
 
 // Symmetric INT4 scale of a group from its max magnitude: fp16(fl32(amax / 7)).
@@ -66,11 +68,28 @@ __device__ __forceinline__ uint16_t int4_scale_bits(float amax) {
   return float_to_half_bits(amax / 7.0f);
 }
 
-// Code in [-8, 7] of one value given the group's fp16 scale (as fp32, nonzero) and 1/scale.
-__device__ __forceinline__ int int4_code(float x, float s, float rcp) {
-  float r = rne_quotient(x, s, rcp);
-  r = __builtin_fminf(__builtin_fmaxf(r, -8.0f), 7.0f);
-  return (int)r;
+// Codes of a whole 64-group, packed eight per dword (even k in the low nibble):
+// q = clamp(rne(fl32(x / s)), -8, 7), biased by 8, converted to bytes (v_cvt_pk_u8_f32),
+// merged pairwise into nibbles and un-biased by flipping bit 3 of every nibble.
+__device__ __forceinline__ void quantize_group_int4(const float* x, float s, uint32_t* packed) {
+  if (s == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) packed[j] = 0u;
+    return;
+  }
+  const float rcp = 1.0f / s;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t ev = 0u, od = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = rne_quotient(x[8 * j + 2 * e], s, rcp);
+      const float b = rne_quotient(x[8 * j + 2 * e + 1], s, rcp);
+      ev = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(a + 8.0f, 0.0f, 15.0f), e, ev);
+      od = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(b + 8.0f, 0.0f, 15.0f), e, od);
+    }
+    packed[j] = ((od << 4) | ev) ^ 0x88888888u;
+  }
 }
 
 // ---------------------------------------------------------------- nibble unpack

@@ -119,7 +119,9 @@ int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K
 
 /*
  * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its
- * cross-token min/max reduction (0 when tokens == 0).
+ * cross-token min/max reduction: one partial (lo, hi) per channel and 320-token chunk (0 when
+ * tokens == 0).  Its contents need no initialization and carry nothing between calls; calls
+ * that share one workspace must not overlap in time (one stream, or one workspace per stream).
  */
 size_t kv_int8_workspace_bytes(int tokens, int channels);
 

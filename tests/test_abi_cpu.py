@@ -85,7 +85,8 @@ def test_gemm_validation(lib):
 def test_kv_validation(lib):
     q = lib.kv_int8_quant
     assert lib.kv_int8_workspace_bytes(0, 4096) == 0
-    assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 160 * 4096 * 4
+    # lo/hi partials of 32 chunks of 320 tokens
+    assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 32 * 4096 * 4
     assert q(FAKE, 16, 12, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
     assert q(FAKE, -1, 16, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
     assert q(FAKE, 16, 16, FAKE, FAKE, FAKE, None, None) == binding.SVDQ_EINVAL

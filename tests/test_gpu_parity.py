@@ -250,7 +250,10 @@ def _gpu_kv(x_bits):
     return q.cpu().numpy(), s.cpu().numpy(), z.cpu().numpy(), host_u16(out)
 
 
-@pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64)])
+# (None,)*3 is the full cache [10240, 32, 128]; 12800 tokens is not a multiple of the 320-token
+# range chunk; (1, 2, 8) is a single token of 16 channels
+@pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64),
+                                   (12800, 32, 128)])
 def test_kv_quant_dequant_bitexact(gpu_lib, shape):
     for name, (x, ref) in kv_case(*shape).items():
         q, s, z, xo = _gpu_kv(x)
@@ -259,6 +262,21 @@ def test_kv_quant_dequant_bitexact(gpu_lib, shape):
         np.testing.assert_array_equal(q, ref["q"])
         bits, _ = okv.dequantize(ref["q"], ref["scale"], ref["zero"])
         np.testing.assert_array_equal(xo, bits)
+
+
+def test_kv_workspace_needs_no_initialization_and_is_reusable(gpu_lib):
+    """A garbage-filled workspace, reused across tensors of different shapes, gives exact codes."""
+    ws = torch.full((B.kv_int8_workspace_bytes(12800, 4096),), 0xA5, dtype=torch.uint8, device="cuda")
+    for shape in [(300, 4, 32), (64, 2, 16), (12800, 32, 128), (300, 4, 32)]:
+        x, ref = kv_case(*shape)["V"]
+        T_, C = x.shape
+        q = torch.empty(T_, C, dtype=torch.uint8, device="cuda")
+        s = torch.empty(C, dtype=torch.float32, device="cuda")
+        z = torch.empty(C, dtype=torch.uint8, device="cuda")
+        B.kv_int8_quant(dev_bf16(x), q, s, z, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(q.cpu().numpy(), ref["q"])
+        np.testing.assert_array_equal(z.cpu().numpy(), ref["zero"])
 
 
 def test_kv_degenerate_channels(gpu_lib):
