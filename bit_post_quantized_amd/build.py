@@ -3,8 +3,10 @@
     python -m bit_post_quantized_amd.build          # compiles every source, always
 
 Flags: -O3, -ffp-contract=off (the kernels place every fused multiply-add explicitly),
-correctly rounded fp32 division, and packed-fp32 instruction generation turned off for the
-device pass (a device feature; the host pass warns that it does not know it, harmlessly).
+correctly rounded fp32 division, packed-fp32 instruction generation turned off for the device
+pass (a device feature; the host pass warns that it does not know it, harmlessly), and MFMA
+results kept in VGPRs (-amdgpu-mfma-vgpr-form): the kernels consume every MFMA result with
+VALU instructions, which cannot read AGPRs without a copy.
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

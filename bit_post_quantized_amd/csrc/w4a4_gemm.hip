@@ -6,145 +6,279 @@
 // partial P[g] = qx[:, g] . qw[g, :] is exact, and
 //     Y = sum_g diag(s_x[g]) P[g] diag(s_w[g]) + bf16(T) L2 + bias.
 //
-// gfx950 mapping.  A 256-thread workgroup computes a 128x128 tile of Y; each of its 4 waves a
-// 64x64 sub-tile made of 4x4 tiles of v_mfma_i32_16x16x64_i8.  One MFMA covers exactly one
-// group (K = 64), so each MFMA result is one P[g] tile: it is converted, scaled by
-// s_x[m] * s_w[n] and accumulated in fp32 registers.  Operands come straight from global memory:
-// lane l reads the 8 packed bytes (16 codes) of row/column l % 16 at k-chunk l / 16 and unpacks
-// them with the x16 trick (see unpack16_x16), so the MFMA yields 256 * P; the 2^-8 is folded
-// into the weight scale (exact).  After the last group, bf16(T) [16 x 32] and L2 [32 x 16]
-// fragments go through v_mfma_f32_16x16x32_bf16 with the fp32 accumulator as C, then the bias
-// is added and the tile is rounded to bf16 (or kept fp32) and stored.
+// gfx950 mapping (one workgroup = 8 waves = a 256 x 256 tile of Y; wave (wm, wn) owns the
+// 128 x 64 sub-tile made of 8 x 4 tiles of 16 x 16):
+//  * Staging.  Per 64-group the tile needs 256 packed rows of xq and 256 packed columns of wq
+//    (32 bytes each).  Every thread loads 16 packed bytes of each with one 16-byte load,
+//    unpacks them to int8 holding 16 * code (see unpack16_x16) and writes them to LDS, so each
+//    code is unpacked once per workgroup rather than once per wave.  Rows are padded to 80
+//    bytes: the 16 lanes that read one MFMA fragment hit 16 disjoint bank quads.  Two LDS
+//    buffers alternate; the next group's global loads are in flight while the current group
+//    is computed, and one barrier per group separates the phases.
+//  * Integer products.  v_mfma_i32_16x16x64_i8 covers exactly one group, so each result is
+//    256 * P[g] for one 16 x 16 tile; operands are single 16-byte LDS reads.
+//  * Scale products.  s_x[m] * s_w[n] is an outer product, which v_mfma_f32_16x16x32_f16
+//    computes exactly (an fp16 x fp16 product is exact in fp32) when only k-slot 0 is nonzero:
+//    lanes 0..15 keep the fp16 scale they read from LDS, lanes 16..63 zero it.
+//    The dequantization is then one convert and one FMA per output and group.  The factor 256
+//    of the unpacked operands is removed once, exactly, in the epilogue.
+//  * Epilogue.  bf16(T) [16 x 32] and L2 [32 x 16] fragments go through
+//    v_mfma_f32_16x16x32_bf16 with the fp32 accumulator as C, then the bias is added and the
+//    tile is rounded to bf16 (or kept fp32) and stored.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
 namespace svdq {
 
-constexpr int BM = 128, BN = 128;
+constexpr int kRowBytes = 80;  // LDS row stride of the unpacked int8 operands (64 + pad)
 
-template <bool OUT_FP32, bool PARTIALS, int NTR>
-__global__ __launch_bounds__(256) void w4a4_gemm_kernel(
+// Tile shape: a workgroup computes TM x TN of Y with (TM / WM) x (TN / WN) waves, each wave a
+// WM x WN sub-tile of 16 x 16 MFMA fragments.
+template <int TM_, int TN_, int WM_, int WN_>
+struct GemmTile {
+  static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_N = TN / WN, WAVES = (TM / WM) * WAVES_N, THREADS = 64 * WAVES;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int kOpA = TM * kRowBytes, kOpB = TN * kRowBytes;
+  static constexpr int kStageBytes = kOpA + kOpB + (TM + TN) * 2;  // A, B, s_x, s_w
+  static constexpr int kLdsBytes = 2 * kStageBytes;                  // double buffer
+  static_assert(2 * TM % THREADS == 0 && 2 * TN % THREADS == 0, "staging split");
+  static_assert(TM + TN == THREADS || TM + TN == 2 * THREADS, "scale staging split");
+};
+
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+
+template <class TL, bool OUT_FP32, bool PARTIALS, int NTR>
+__global__ __launch_bounds__(TL::THREADS) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ x_scales,
     const float* __restrict__ T, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ w_scales, const uint16_t* __restrict__ L2,
     const uint16_t* __restrict__ bias, int M, int N, int K, void* __restrict__ Y,
     int32_t* __restrict__ P) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int r = 16 * NTR;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rl = lane & 15;
-  const int kc = lane >> 4;
-  const int m0 = blockIdx.y * BM + (wave >> 1) * 64;
-  const int n0 = blockIdx.x * BN + (wave & 1) * 64;
+  constexpr int TM = TL::TM, TN = TL::TN, WM = TL::WM, WN = TL::WN, FM = TL::FM, FN = TL::FN;
+  constexpr int kOpA = TL::kOpA, kOpB = TL::kOpB, kStageBytes = TL::kStageBytes;
+  constexpr int NT = TL::THREADS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WAVES_N, wn = wave % TL::WAVES_N;
+  const int rl = lane & 15, kc = lane >> 4;
+  const int m_tile = blockIdx.y * TM, n_tile = blockIdx.x * TN;
   const int G = K / kGroup;
   const size_t ldq = (size_t)(K / 2);
 
-  // operand rows / columns owned by this lane (clamped so every load stays in bounds)
-  const uint8_t* arow[4];
-  const uint8_t* bcol[4];
-  int srow[4][4];  // output rows of this lane: m0 + 16 i + 4 kc + e
-  int scol[4];     // output columns of this lane: n0 + 16 j + rl
+  // ---- staging: segment s of an operand tile is the 16 packed bytes [16 (s & 1), +16) of row
+  //      (or column) s / 2; thread t moves segments t, t + NT, ... of A and of B
+  constexpr int SA_PER = 2 * TM / NT, SB_PER = 2 * TN / NT;
+  const uint8_t* a_src[SA_PER];
+  const uint8_t* b_src[SB_PER];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = min(m0 + 16 * i + rl, M - 1);
-    arow[i] = xq + (size_t)ra * ldq + kc * 8;
-    const int cb = min(n0 + 16 * i + rl, N - 1);
-    bcol[i] = wq + (size_t)cb * ldq + kc * 8;
-    scol[i] = n0 + 16 * i + rl;
+  for (int u = 0; u < SA_PER; ++u) {
+    const int sg = tid + u * NT;
+    a_src[u] = xq + (size_t)min(m_tile + (sg >> 1), M - 1) * ldq + (sg & 1) * 16;
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) srow[i][e] = m0 + 16 * i + 4 * kc + e;
+  for (int u = 0; u < SB_PER; ++u) {
+    const int sg = tid + u * NT;
+    b_src[u] = wq + (size_t)min(n_tile + (sg >> 1), N - 1) * ldq + (sg & 1) * 16;
+  }
+  // scale staging: entries 0..TM-1 are s_x of the tile's rows, TM..TM+TN-1 s_w of its columns
+  constexpr int SS_PER = (TM + TN) / NT;
+  const uint16_t* s_src[SS_PER];
+  size_t s_stride[SS_PER];
+#pragma unroll
+  for (int u = 0; u < SS_PER; ++u) {
+    const int e = tid + u * NT;
+    const bool is_a = e < TM;
+    s_src[u] = PARTIALS ? nullptr
+               : is_a ? x_scales + min(m_tile + e, M - 1)
+                      : w_scales + min(n_tile + e - TM, N - 1);
+    s_stride[u] = is_a ? (size_t)M : (size_t)N;
   }
 
-  v4f acc[4][4];
+  auto stage_ptr = [&](int buf) { return lds + buf * kStageBytes; };
+  auto store_stage = [&](int buf, const v4u* a, const v4u* b, const uint16_t* sc) {
+    uint8_t* st = stage_ptr(buf);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int u = 0; u < SA_PER; ++u) {
+      const int sg = tid + u * NT;
+      uint8_t* d = st + (sg >> 1) * kRowBytes + (sg & 1) * 32;
+      reinterpret_cast<v4i*>(d)[0] = unpack16_x16(v2u{a[u].x, a[u].y});
+      reinterpret_cast<v4i*>(d)[1] = unpack16_x16(v2u{a[u].z, a[u].w});
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < SB_PER; ++u) {
+      const int sg = tid + u * NT;
+      uint8_t* d = st + kOpA + (sg >> 1) * kRowBytes + (sg & 1) * 32;
+      reinterpret_cast<v4i*>(d)[0] = unpack16_x16(v2u{b[u].x, b[u].y});
+      reinterpret_cast<v4i*>(d)[1] = unpack16_x16(v2u{b[u].z, b[u].w});
+    }
+#pragma unroll
+    for (int u = 0; u < SS_PER; ++u)
+      reinterpret_cast<uint16_t*>(st + kOpA + kOpB)[tid + u * NT] = sc[u];
+  };
+
+  // ---- per-lane fragment addresses (byte offsets inside a stage)
+  // A fragment i: rows wm*128 + 16 i + rl, k-chunk kc; B fragment j: columns wn*64 + 16 j + rl
+  const int a_frag = (wm * WM + rl) * kRowBytes + kc * 16;
+  const int b_frag = kOpA + (wn * WN + rl) * kRowBytes + kc * 16;
+  // scale operands: every lane reads its row's / column's fp16 scale; only lanes 0..15 (k-slot
+  // 0 of the outer-product MFMA) keep it, the others contribute zero
+  const int sa_off = kOpA + kOpB + (wm * WM + rl) * 2;
+  const int sb_off = kOpA + kOpB + TM * 2 + (wn * WN + rl) * 2;
+  const uint32_t s_keep = kc == 0 ? 0xFFFFu : 0u;
+
+  v4f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: group 0 into buffer 0
+  {
+    v4u a[SA_PER], b[SB_PER];
+    uint16_t sc[SS_PER];
+#pragma unroll
+    for (int u = 0; u < SA_PER; ++u) a[u] = *reinterpret_cast<const v4u*>(a_src[u]);
+#pragma unroll
+    for (int u = 0; u < SB_PER; ++u) b[u] = *reinterpret_cast<const v4u*>(b_src[u]);
+#pragma unroll
+    for (int u = 0; u < SS_PER; ++u) sc[u] = PARTIALS ? 0 : *s_src[u];
+    store_stage(0, a, b, sc);
+    __syncthreads();
+  }
 
   for (int g = 0; g < G; ++g) {
-    v4i A[4], B[4];
+    const int buf = g & 1;
+    v4u a_next[SA_PER], b_next[SB_PER];
+    uint16_t s_next[SS_PER];
+    const bool more = g + 1 < G;
+    if (more) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A[i] = unpack16_x16(*reinterpret_cast<const v2u*>(arow[i] + g * 32));
-      B[i] = unpack16_x16(*reinterpret_cast<const v2u*>(bcol[i] + g * 32));
+      for (int u = 0; u < SA_PER; ++u) a_next[u] = *reinterpret_cast<const v4u*>(a_src[u] + (size_t)(g + 1) * 32);
+#pragma unroll
+      for (int u = 0; u < SB_PER; ++u) b_next[u] = *reinterpret_cast<const v4u*>(b_src[u] + (size_t)(g + 1) * 32);
+#pragma unroll
+      for (int u = 0; u < SS_PER; ++u) s_next[u] = PARTIALS ? 0 : s_src[u][(size_t)(g + 1) * s_stride[u]];
     }
-    if constexpr (PARTIALS) {
+    const uint8_t* st = stage_ptr(buf);
+
+    v4i B[FN];
+    v8h_t SB[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < FN; ++j) {
+      B[j] = *reinterpret_cast<const v4i*>(st + b_frag + j * 16 * kRowBytes);
+      const uint32_t sw = *reinterpret_cast<const uint16_t*>(st + sb_off + j * 32) & s_keep;
+      SB[j] = __builtin_bit_cast(v8h_t, v4u{sw, 0u, 0u, 0u});
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], B[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+    for (int i = 0; i < FM; ++i) {
+      const v4i A = *reinterpret_cast<const v4i*>(st + a_frag + i * 16 * kRowBytes);
+      if constexpr (PARTIALS) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (srow[i][e] < M && scol[j] < N)
-              P[((size_t)g * M + srow[i][e]) * N + scol[j]] = p[e] >> 8;  // exact: 256 * P
+        for (int j = 0; j < FN; ++j) {
+          const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+          const int col = n_tile + wn * WN + 16 * j + rl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = m_tile + wm * WM + 16 * i + 4 * kc + e;
+            if (row < M && col < N) P[((size_t)g * M + row) * N + col] = p[e] >> 8;  // exact
+          }
         }
-    } else {
-      float sx[4][4], sw[4];
+      } else {
+        const uint32_t sx = *reinterpret_cast<const uint16_t*>(st + sa_off + i * 32) & s_keep;
+        const v8h_t SA = __builtin_bit_cast(v8h_t, v4u{sx, 0u, 0u, 0u});
+        v4i p[FN];
+        v4f sp[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < FN; ++j) {
+          p[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+          sp[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(SA, SB[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sx[i][e] = half_bits_to_float(x_scales[(size_t)g * M + min(srow[i][e], M - 1)]);
-        sw[i] = half_bits_to_float(w_scales[(size_t)g * N + min(scol[i], N - 1)]) * 0x1p-8f;
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf((float)p[j][e], sp[j][e], acc[i][j][e]);
+          // pin the dequantization of this fragment here: otherwise the optimizer sinks every
+          // FMA below the last MFMA of the group and all MFMA results are live at once
+          asm volatile("" : "+v"(acc[i][j]));
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], B[j], v4i{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][j][e] = __builtin_fmaf((float)p[e], sx[i][e] * sw[j], acc[i][j][e]);
-        }
+      // and keep the machine scheduler from hoisting the next fragment's MFMAs over this
+      // fragment's dequantization
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (more) store_stage(buf ^ 1, a_next, b_next, s_next);
+    __syncthreads();
   }
   if constexpr (PARTIALS) return;
 
-  // ---- fused epilogue: low-rank up-projection (bf16 MFMA, fp32 accumulator as C) and bias
+  // ---- epilogue: remove the 256 of the unpacked operands, low-rank up-projection, bias
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] *= 0x1p-8f;
+  // The epilogue's addresses are loop-invariant; computed before the K loop they would stay
+  // live across it and spill.  An opaque copy of the indices keeps them here.
+  int row0 = m_tile + wm * WM, col0 = n_tile + wn * WN, Mo = M, No = N;
+  asm volatile("" : "+v"(row0), "+v"(col0), "+s"(Mo), "+s"(No));
   if constexpr (NTR > 0) {
 #pragma unroll
     for (int rk = 0; rk < (r + 31) / 32; ++rk) {
       const int kk = rk * 32 + kc * 8;  // this lane's 8 rank indices
       const bool kv = kk < r;
-      v8bf At[4], Bt[4];
+      v8bf Bt[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4u a = v4u{0u, 0u, 0u, 0u}, b = v4u{0u, 0u, 0u, 0u};
+      for (int j = 0; j < FN; ++j) {
+        v4u b = v4u{0u, 0u, 0u, 0u};
+        if (kv) b = *reinterpret_cast<const v4u*>(L2 + (size_t)min(col0 + 16 * j + rl, No - 1) * r + kk);
+        Bt[j] = __builtin_bit_cast(v8bf, b);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        v4u a = v4u{0u, 0u, 0u, 0u};
         if (kv) {
-          const v4f* tp = reinterpret_cast<const v4f*>(T + (size_t)min(m0 + 16 * i + rl, M - 1) * r + kk);
+          const v4f* tp = reinterpret_cast<const v4f*>(T + (size_t)min(row0 + 16 * i + rl, Mo - 1) * r + kk);
           const v4f t0 = tp[0], t1 = tp[1];
           a = v4u{pack2_bf16(t0.x, t0.y), pack2_bf16(t0.z, t0.w), pack2_bf16(t1.x, t1.y),
                   pack2_bf16(t1.z, t1.w)};
-          b = *reinterpret_cast<const v4u*>(L2 + (size_t)min(n0 + 16 * i + rl, N - 1) * r + kk);
         }
-        At[i] = __builtin_bit_cast(v8bf, a);
-        Bt[i] = __builtin_bit_cast(v8bf, b);
+        const v8bf At = __builtin_bit_cast(v8bf, a);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(At, Bt[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(At[i], Bt[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float bj = bias ? bf16_bits_to_float(bias[min(scol[j], N - 1)]) : 0.0f;
+  for (int j = 0; j < FN; ++j) {
+    const int col = col0 + 16 * j + rl;
+    const float bj = bias ? bf16_bits_to_float(bias[min(col, No - 1)]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = srow[i][e], col = scol[j];
-        if (row < M && col < N) {
+        const int row = row0 + 16 * i + 4 * kc + e;
+        if (row < Mo && col < No) {
           const float v = acc[i][j][e] + bj;
           if constexpr (OUT_FP32)
-            reinterpret_cast<float*>(Y)[(size_t)row * N + col] = v;
+            reinterpret_cast<float*>(Y)[(size_t)row * No + col] = v;
           else
-            reinterpret_cast<uint16_t*>(Y)[(size_t)row * N + col] = float_to_bf16_bits(v);
+            reinterpret_cast<uint16_t*>(Y)[(size_t)row * No + col] = float_to_bf16_bits(v);
         }
       }
   }
+}
+
+// Tile used for every launch (see the design notes at the top of the file).
+using Tile = GemmTile<128, 128, 64, 64>;
+
+// The double-buffered stage may need more than the default 64 KB of dynamic LDS.
+template <typename F>
+static hipError_t allow_lds(F kernel) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile::kLdsBytes);
 }
 
 template <bool OUT_FP32, bool PARTIALS>
@@ -153,11 +287,15 @@ static hipError_t launch_ntr(int ntr, dim3 grid, hipStream_t stream, const uint8
                              const uint16_t* w_scales, const uint16_t* L2, const uint16_t* bias,
                              int M, int N, int K, void* Y, int32_t* P) {
   switch (ntr) {
-#define SVDQ_GEMM_CASE(n)                                                                    \
-  case n:                                                                                    \
-    hipLaunchKernelGGL((w4a4_gemm_kernel<OUT_FP32, PARTIALS, n>), grid, dim3(256), 0, stream, \
-                       xq, x_scales, T, wq, w_scales, L2, bias, M, N, K, Y, P);              \
-    break;
+#define SVDQ_GEMM_CASE(n)                                                                       \
+  case n: {                                                                                     \
+    const hipError_t e = allow_lds(w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n>);              \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL((w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n>), grid,                   \
+                       dim3(Tile::THREADS), Tile::kLdsBytes, stream, xq, x_scales, T, wq,       \
+                       w_scales, L2, bias, M, N, K, Y, P);                                      \
+    break;                                                                                      \
+  }
     SVDQ_GEMM_CASE(0)
     SVDQ_GEMM_CASE(1)
     SVDQ_GEMM_CASE(2)
@@ -178,7 +316,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const f
                             const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
                             const uint16_t* bias, int M, int N, int K, int r, void* Y,
                             int out_fp32, int32_t* partials, hipStream_t stream) {
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  dim3 grid((N + Tile::TN - 1) / Tile::TN, (M + Tile::TM - 1) / Tile::TM);
   if (partials)
     return launch_ntr<false, true>(0, grid, stream, xq, nullptr, nullptr, wq, nullptr, nullptr,
                                    nullptr, M, N, K, nullptr, partials);
