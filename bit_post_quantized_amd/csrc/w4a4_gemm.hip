@@ -25,6 +25,8 @@
 //  * Epilogue.  bf16(T) [16 x 32] and L2 [32 x 16] fragments go through
 //    v_mfma_f32_16x16x32_bf16 with the fp32 accumulator as C, then the bias is added and the
 //    tile is rounded to bf16 (or kept fp32) and stored.
+#include <type_traits>
+
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
@@ -33,10 +35,14 @@ namespace svdq {
 constexpr int kRowBytes = 80;  // LDS row stride of the unpacked int8 operands (64 + pad)
 
 // Tile shape: a workgroup computes TM x TN of Y with (TM / WM) x (TN / WN) waves, each wave a
-// WM x WN sub-tile of 16 x 16 MFMA fragments.
-template <int TM_, int TN_, int WM_, int WN_>
+// WM x WN sub-tile of 16 x 16 MFMA fragments; PREFETCH groups of packed operands are in flight
+// in registers ahead of the LDS stage being computed.
+template <int TM_, int TN_, int WM_, int WN_, int PREFETCH_, int WAVES_PER_EU_>
 struct GemmTile {
   static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+  static constexpr int PREFETCH = PREFETCH_;  // groups in flight between global memory and LDS
+  static constexpr int WAVES_PER_EU = WAVES_PER_EU_;  // occupancy the register budget must allow
+  static_assert(PREFETCH >= 1 && PREFETCH <= 3, "prefetch depth");
   static constexpr int WAVES_N = TN / WN, WAVES = (TM / WM) * WAVES_N, THREADS = 64 * WAVES;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int kOpA = TM * kRowBytes, kOpB = TN * kRowBytes;
@@ -49,7 +55,8 @@ struct GemmTile {
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 
 template <class TL, bool OUT_FP32, bool PARTIALS, int NTR>
-__global__ __launch_bounds__(TL::THREADS) void w4a4_gemm_kernel(
+__global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
+void w4a4_gemm_kernel(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ x_scales,
     const float* __restrict__ T, const uint8_t* __restrict__ wq,
     const uint16_t* __restrict__ w_scales, const uint16_t* __restrict__ L2,
@@ -135,34 +142,29 @@ __global__ __launch_bounds__(TL::THREADS) void w4a4_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: group 0 into buffer 0
-  {
-    v4u a[SA_PER], b[SB_PER];
-    uint16_t sc[SS_PER];
+  // ---- global -> register prefetch ring of PD groups (slot = group % PD); LDS double buffer
+  constexpr int PD = TL::PREFETCH;
+  v4u ra[PD][SA_PER], rb[PD][SB_PER];
+  uint16_t rs[PD][SS_PER];
+  auto load_group = [&](int gg, v4u* a, v4u* b, uint16_t* sc) {
 #pragma unroll
-    for (int u = 0; u < SA_PER; ++u) a[u] = *reinterpret_cast<const v4u*>(a_src[u]);
+    for (int u = 0; u < SA_PER; ++u) a[u] = *reinterpret_cast<const v4u*>(a_src[u] + (size_t)gg * 32);
 #pragma unroll
-    for (int u = 0; u < SB_PER; ++u) b[u] = *reinterpret_cast<const v4u*>(b_src[u]);
+    for (int u = 0; u < SB_PER; ++u) b[u] = *reinterpret_cast<const v4u*>(b_src[u] + (size_t)gg * 32);
 #pragma unroll
-    for (int u = 0; u < SS_PER; ++u) sc[u] = PARTIALS ? 0 : *s_src[u];
-    store_stage(0, a, b, sc);
-    __syncthreads();
-  }
+    for (int u = 0; u < SS_PER; ++u) sc[u] = PARTIALS ? 0 : s_src[u][(size_t)gg * s_stride[u]];
+  };
+#pragma unroll
+  for (int k = 0; k < PD; ++k)
+    if (k < G) load_group(k, ra[k], rb[k], rs[k]);
+  store_stage(0, ra[0], rb[0], rs[0]);
+  __syncthreads();
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    v4u a_next[SA_PER], b_next[SB_PER];
-    uint16_t s_next[SS_PER];
-    const bool more = g + 1 < G;
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < SA_PER; ++u) a_next[u] = *reinterpret_cast<const v4u*>(a_src[u] + (size_t)(g + 1) * 32);
-#pragma unroll
-      for (int u = 0; u < SB_PER; ++u) b_next[u] = *reinterpret_cast<const v4u*>(b_src[u] + (size_t)(g + 1) * 32);
-#pragma unroll
-      for (int u = 0; u < SS_PER; ++u) s_next[u] = PARTIALS ? 0 : s_src[u][(size_t)(g + 1) * s_stride[u]];
-    }
-    const uint8_t* st = stage_ptr(buf);
+  // one K step: group g is in LDS buffer g & 1 and its ring slot PH is free again
+  auto step = [&](int g, auto ph) {
+    constexpr int PH = decltype(ph)::value, NX = (PH + 1) % PD;
+    if (g + PD < G) load_group(g + PD, ra[PH], rb[PH], rs[PH]);
+    const uint8_t* st = stage_ptr(g & 1);
 
     v4i B[FN];
     v8h_t SB[FN];
@@ -209,8 +211,13 @@ __global__ __launch_bounds__(TL::THREADS) void w4a4_gemm_kernel(
       // fragment's dequantization
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) store_stage(buf ^ 1, a_next, b_next, s_next);
+    if (g + 1 < G) store_stage((g + 1) & 1, ra[NX], rb[NX], rs[NX]);
     __syncthreads();
+  };
+  for (int g = 0; g < G; g += PD) {
+    step(g, std::integral_constant<int, 0>{});
+    if constexpr (PD > 1) if (g + 1 < G) step(g + 1, std::integral_constant<int, 1 % PD>{});
+    if constexpr (PD > 2) if (g + 2 < G) step(g + 2, std::integral_constant<int, 2 % PD>{});
   }
   if constexpr (PARTIALS) return;
 
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(TL::THREADS) void w4a4_gemm_kernel(
 }
 
 // Tile used for every launch (see the design notes at the top of the file).
-using Tile = GemmTile<128, 128, 64, 64>;
+using Tile = GemmTile<128, 128, 64, 64, 2, 3>;
 
 // The double-buffered stage may need more than the default 64 KB of dynamic LDS.
 template <typename F>
