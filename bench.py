@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=384,
+    ap.add_argument("--cpu-rows", type=int, default=M,
                     help="token rows of the oracle's CPU baseline sample")
     return ap.parse_args()
 
