@@ -133,6 +133,69 @@ def pack_weights(R32: np.ndarray) -> dict:
     return dict(wq=pack_nibbles(codes), s_w=np.ascontiguousarray(s16.T), codes=codes)
 
 
+# --------------------------------------------------------------------------- BF6 container
+# FLUX4 3.2: on newer GPUs the matrix units read a small floating-point format directly, which
+# removes the 4-bit unpack step that INT4 needs on INT8 units (W4A8 2.2).  The format with that
+# property on the target GPU is BF6 = E3M2 as defined by the OCP Microscaling (MX) format
+# specification v1.0 [external]: sign bit 5, exponent bits 4..2 with bias 3, mantissa bits
+# 1..0; exponent 0 encodes the subnormals 2^-2 * m / 4.  Every integer in [-8, 8] is exactly
+# representable, so the method's INT4 codes travel in it unchanged: only the container differs.
+E3M2_BIAS = 3
+
+
+def e3m2_value(bits) -> np.ndarray:
+    """Value (float64) of each 6-bit E3M2 pattern, from the format definition."""
+    b = np.asarray(bits, dtype=np.int64) & 0x3F
+    sign = np.where(b >> 5, -1.0, 1.0)
+    e = (b >> 2) & 0x7
+    m = (b & 0x3).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 4.0, (e - E3M2_BIAS).astype(np.int64))
+    sub = np.ldexp(m / 4.0, 1 - E3M2_BIAS)
+    return sign * np.where(e == 0, sub, normal)
+
+
+def e3m2_encode_codes(codes) -> np.ndarray:
+    """Exact E3M2 pattern (uint8, 6 significant bits) of each integer code; zero encodes as +0.
+
+    Raises ValueError for an integer the format cannot hold exactly (|c| > 8 or c = 9, 11, ...).
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    a = np.abs(c)
+    out = np.zeros(c.shape, dtype=np.uint8)
+    nz = a > 0
+    e = np.zeros(c.shape, dtype=np.int64)
+    e[nz] = np.floor(np.log2(a[nz])).astype(np.int64)
+    frac = np.zeros(c.shape, dtype=np.float64)
+    frac[nz] = a[nz] / np.ldexp(1.0, e[nz]) - 1.0          # in [0, 1)
+    m = np.rint(frac * 4.0).astype(np.int64)
+    exact = (~nz) | ((e + E3M2_BIAS <= 7) & (m < 4) & (frac * 4.0 == m))
+    if not np.all(exact):
+        raise ValueError("code not exactly representable in E3M2")
+    out[nz] = (((c[nz] < 0).astype(np.int64) << 5) | ((e[nz] + E3M2_BIAS) << 2) | m[nz]).astype(np.uint8)
+    return out
+
+
+def pack_e3m2(codes: np.ndarray) -> np.ndarray:
+    """[rows, K] int codes -> [rows, 3K/4] bytes: the codes' E3M2 patterns in k order, 6 bits
+    each, as one little-endian bit stream per row (code k holds stream bits 6k .. 6k+5)."""
+    pat = e3m2_encode_codes(codes)
+    rows, K = pat.shape
+    bits = ((pat[..., None] >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8)  # [rows, K, 6]
+    return np.packbits(bits.reshape(rows, 6 * K), axis=1, bitorder="little")
+
+
+def unpack_e3m2(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of ``pack_e3m2``: [rows, 3K/4] bytes -> [rows, K] int codes (values must be
+    integers, as they are for every packed code)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    bits = np.unpackbits(p, axis=1, bitorder="little")[:, : 6 * K].reshape(p.shape[0], K, 6)
+    pat = (bits.astype(np.int64) << np.arange(6)).sum(axis=2)
+    v = e3m2_value(pat)
+    if not np.all(v == np.rint(v)):
+        raise ValueError("packed value is not an integer code")
+    return v.astype(np.int8)
+
+
 # --------------------------------------------------------------------------- activations
 def smooth_activations(X_bits, inv_lam32: np.ndarray) -> np.ndarray:
     """X^ = fl32(fl32(X) * inv_lam): the smoothing divide as one fp32 multiply by the stored
