@@ -24,7 +24,8 @@ LIB = os.path.join(LIBDIR, "libsvdq.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "pack_weights.hip", "act_quant.hip", "w4a4_gemm.hip", "kv_int8.hip"]
+SOURCES = ["abi.cpp", "pack_weights.hip", "act_quant.hip", "w4a4_gemm.hip", "w4a4_gemm_e3m2.hip",
+           "kv_int8.hip"]
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

@@ -71,20 +71,31 @@ const char* svdq_status_str(int status) {
 
 const char* svdq_last_error(void) { return g_last_error; }
 
-int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
-                      void* stream) {
+static int pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
+                        void* stream, int e3m2, const char* name) {
   if (int s = check_k(K)) return s;
   if (N <= 0) return fail(SVDQ_EINVAL, "N must be positive (got %d)", N);
   if ((long long)K * N > kMaxElems) return fail(SVDQ_ESHAPE, "K * N too large");
   if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535");
   if (!R || !wq || !w_scales) return fail(SVDQ_EINVAL, "NULL pointer");
   if (!aligned16(R) || !aligned16(wq)) return fail(SVDQ_EALIGN, "R and wq must be 16-byte aligned");
-  return hip_status(svdq::launch_pack_weights(R, K, N, wq, w_scales, (hipStream_t)stream),
-                    "svdq_pack_weights");
+  return hip_status(svdq::launch_pack_weights(R, K, N, wq, w_scales, e3m2, (hipStream_t)stream),
+                    name);
 }
 
-int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
-                      int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream) {
+int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
+                      void* stream) {
+  return pack_weights(R, K, N, wq, w_scales, stream, 0, "svdq_pack_weights");
+}
+
+int svdq_pack_weights_e3m2(const float* R, int K, int N, uint8_t* wq6, uint16_t* w_scales,
+                           void* stream) {
+  return pack_weights(R, K, N, wq6, w_scales, stream, 1, "svdq_pack_weights_e3m2");
+}
+
+static int quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                        int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream,
+                        int e3m2, const char* name) {
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0 (got %d)", M);
   if (int s = check_k(K)) return s;
   if (int s = check_rank(r)) return s;
@@ -94,9 +105,22 @@ int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t
   if (!aligned16(X) || !aligned16(inv_lambda) || !aligned16(xq) || (r > 0 && !aligned16(L1)))
     return fail(SVDQ_EALIGN, "X, inv_lambda, xq and L1 must be 16-byte aligned");
   if (M == 0) return ok();
-  return hip_status(svdq::launch_quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T,
+  return hip_status(svdq::launch_quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, e3m2,
                                               (hipStream_t)stream),
-                    "svdq_quantize_act");
+                    name);
+}
+
+int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                      int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream) {
+  return quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream, 0,
+                      "svdq_quantize_act");
+}
+
+int svdq_quantize_act_e3m2(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                           int M, int K, int r, uint8_t* xq6, uint16_t* x_scales, float* T,
+                           void* stream) {
+  return quantize_act(X, inv_lambda, L1, M, K, r, xq6, x_scales, T, stream, 1,
+                      "svdq_quantize_act_e3m2");
 }
 
 static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K) {
@@ -111,10 +135,15 @@ static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K)
   return SVDQ_OK;
 }
 
-int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
-                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
-                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
-                   void* stream) {
+typedef hipError_t (*gemm_launcher)(const uint8_t*, const uint16_t*, const float*,
+                                    const uint8_t*, const uint16_t*, const uint16_t*,
+                                    const uint16_t*, int, int, int, int, void*, int, int32_t*,
+                                    hipStream_t);
+
+static int gemm(gemm_launcher launch, const char* name, const uint8_t* xq,
+                const uint16_t* x_scales, const float* T, const uint8_t* wq,
+                const uint16_t* w_scales, const uint16_t* L2, const uint16_t* bias, int M, int N,
+                int K, int r, void* Y, int out_dtype, void* stream) {
   if (int s = check_gemm(xq, wq, M, N, K)) return s;
   if (int s = check_rank(r)) return s;
   if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_FP32)
@@ -124,20 +153,46 @@ int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
   if (!aligned16(Y) || (r > 0 && (!aligned16(T) || !aligned16(L2))))
     return fail(SVDQ_EALIGN, "Y, T and L2 must be 16-byte aligned");
   if (M == 0) return ok();
-  return hip_status(svdq::launch_w4a4_gemm(xq, x_scales, T, wq, w_scales, L2, bias, M, N, K, r,
-                                           Y, out_dtype == SVDQ_OUT_FP32, nullptr,
-                                           (hipStream_t)stream),
-                    "svdq_w4a4_gemm");
+  return hip_status(launch(xq, x_scales, T, wq, w_scales, L2, bias, M, N, K, r, Y,
+                           out_dtype == SVDQ_OUT_FP32, nullptr, (hipStream_t)stream),
+                    name);
+}
+
+static int partials(gemm_launcher launch, const char* name, const uint8_t* xq,
+                    const uint8_t* wq, int M, int N, int K, int32_t* P, void* stream) {
+  if (int s = check_gemm(xq, wq, M, N, K)) return s;
+  if (!P) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (M == 0) return ok();
+  return hip_status(launch(xq, nullptr, nullptr, wq, nullptr, nullptr, nullptr, M, N, K, 0,
+                           nullptr, 0, P, (hipStream_t)stream),
+                    name);
+}
+
+int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
+                   void* stream) {
+  return gemm(svdq::launch_w4a4_gemm, "svdq_w4a4_gemm", xq, x_scales, T, wq, w_scales, L2,
+              bias, M, N, K, r, Y, out_dtype, stream);
+}
+
+int svdq_w4a4_gemm_e3m2(const uint8_t* xq6, const uint16_t* x_scales, const float* T,
+                        const uint8_t* wq6, const uint16_t* w_scales, const uint16_t* L2,
+                        const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                        int out_dtype, void* stream) {
+  return gemm(svdq::launch_w4a4_gemm_e3m2, "svdq_w4a4_gemm_e3m2", xq6, x_scales, T, wq6,
+              w_scales, L2, bias, M, N, K, r, Y, out_dtype, stream);
 }
 
 int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int32_t* P,
                        void* stream) {
-  if (int s = check_gemm(xq, wq, M, N, K)) return s;
-  if (!P) return fail(SVDQ_EINVAL, "NULL pointer");
-  if (M == 0) return ok();
-  return hip_status(svdq::launch_w4a4_gemm(xq, nullptr, nullptr, wq, nullptr, nullptr, nullptr,
-                                           M, N, K, 0, nullptr, 0, P, (hipStream_t)stream),
-                    "svdq_w4a4_partials");
+  return partials(svdq::launch_w4a4_gemm, "svdq_w4a4_partials", xq, wq, M, N, K, P, stream);
+}
+
+int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N, int K,
+                            int32_t* P, void* stream) {
+  return partials(svdq::launch_w4a4_gemm_e3m2, "svdq_w4a4_partials_e3m2", xq6, wq6, M, N, K, P,
+                  stream);
 }
 
 size_t kv_int8_workspace_bytes(int tokens, int channels) {

@@ -6,22 +6,30 @@
 // scale per token and 64-group).  SVDQ / DCMP: the branch is fused so the activations are read
 // from HBM once.
 //
-// Work decomposition.  A workgroup owns 16 tokens (rows).  K is cut into strips of 256
-// (four 64-groups); the (up to 8) waves of the workgroup take strips round-robin.  Inside a strip, lane
-// l holds row (l % 16) and group (l / 16) of the strip: it loads that group's 64 bf16 values
-// (128 contiguous bytes), smooths them, finds the group max in-lane (no shuffles), quantizes and
-// writes its 32 packed bytes and its scale.  The same registers, rounded to bf16, are the A
-// operand of v_mfma_f32_16x16x32_bf16: in MFMA step j (0..7) lane group q supplies k = 64q+8j+i,
-// and the B operand (L1, stored K-contiguous) is loaded with the same k map, so the 8 MFMAs of
-// a strip sum exactly the strip's 256 k.  Per-wave partial T tiles are summed in LDS in wave
-// order (deterministic) and written once.
+// Work decomposition.  A workgroup owns 16 tokens (rows) and all of K; its waves take the
+// 64-groups round-robin.  In a group, lane l holds row l % 16 and the 16 consecutive k
+// [16 q, 16 q + 16) of quarter q = l / 16: two 16-byte loads, so every load instruction reads
+// 16 rows x 64 contiguous bytes.  The loads of kActBatch groups are issued before any of them is
+// used.  The group max is folded over the four quarter lanes of a row with two lane shuffles;
+// every lane then codes its 16 values (exact quotient, no division per element) and writes
+// them as 8 bytes of nibbles or 12 bytes of BF6 (E3M2) codes -- the two containers the GEMMs
+// read -- and the quarter-0 lanes write the 16 rows' scales (32 contiguous bytes).
+// Low-rank branch: the same registers rounded to bf16 are the A operand of two
+// v_mfma_f32_16x16x32_bf16 per group (k-slots 8 (l / 16) + i of the MFMA take k = 16 q + i and
+// 16 q + 8 + i), and L1, stored K-contiguous, is loaded with the same k map, so the MFMAs sum
+// exactly the group's 64 k.  Per-wave partial T tiles are summed in LDS in wave order
+// (deterministic) and written once.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
 namespace svdq {
 
-template <int NTR>  // number of 16-wide tiles of the rank r (r = 16 * NTR)
-__global__ __launch_bounds__(512) void quantize_act_kernel(
+constexpr int kActRows = 16;   // tokens per workgroup
+constexpr int kActBatch = 6;   // groups per wave whose loads are in flight together
+constexpr int kActMaxWaves = 8;
+
+template <int NTR, bool E3M2>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
+__global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
     uint16_t* __restrict__ x_scales, float* __restrict__ T) {
@@ -32,69 +40,97 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
   const int nwaves = blockDim.x >> 6;
   const int rl = lane & 15;
   const int q = lane >> 4;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = blockIdx.x * kActRows;
   const int row = row0 + rl;
   const int row_ld = row < M ? row : M - 1;
   const int G = K / kGroup;
-  const int nstrips = (G + 3) / 4;
+  const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
+  const size_t ldq = E3M2 ? (size_t)K / 4 * 3 : (size_t)K / 2;
 
   v4f acc[NTR > 0 ? NTR : 1];
 #pragma unroll
   for (int t = 0; t < (NTR > 0 ? NTR : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int strip = wave; strip < nstrips; strip += nwaves) {
-    const int g = strip * 4 + q;
-    const bool valid = g < G;
-    const int k0 = (valid ? g : G - 1) * kGroup;  // loads stay in bounds; invalid lanes zeroed
-    float xh[kGroup];
-    {
-      const v4u* xs = reinterpret_cast<const v4u*>(X + (size_t)row_ld * K + k0);
-      const v4f* ls = reinterpret_cast<const v4f*>(inv_lambda + k0);
-      const float keep = valid ? 1.0f : 0.0f;
+  for (int j0 = wave; j0 < G; j0 += kActBatch * nwaves) {
+    v4u raw[kActBatch][2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v4u w = xs[c];
-        const v4f l0 = ls[2 * c] * keep, l1 = ls[2 * c + 1] * keep;
-        xh[8 * c + 0] = __uint_as_float(w.x << 16) * l0.x;
-        xh[8 * c + 1] = __uint_as_float(w.x & 0xFFFF0000u) * l0.y;
-        xh[8 * c + 2] = __uint_as_float(w.y << 16) * l0.z;
-        xh[8 * c + 3] = __uint_as_float(w.y & 0xFFFF0000u) * l0.w;
-        xh[8 * c + 4] = __uint_as_float(w.z << 16) * l1.x;
-        xh[8 * c + 5] = __uint_as_float(w.z & 0xFFFF0000u) * l1.y;
-        xh[8 * c + 6] = __uint_as_float(w.w << 16) * l1.z;
-        xh[8 * c + 7] = __uint_as_float(w.w & 0xFFFF0000u) * l1.w;
-      }
+    for (int b = 0; b < kActBatch; ++b) {  // unconditional loads (group index clamped)
+      const int g = min(j0 + b * nwaves, G - 1);
+      const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
+      raw[b][0] = p[0];
+      raw[b][1] = p[1];
     }
-
-    // ---- INT4 quantization of this lane's group
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
-    const uint16_t sb = int4_scale_bits(amax);
-    const float s = half_bits_to_float(sb);
-    uint32_t packed[8];
-    quantize_group_int4(xh, s, packed);
-    if (valid && row < M) {
-      v4u* dst = reinterpret_cast<v4u*>(xq + (size_t)row * (K / 2) + (size_t)g * (kGroup / 2));
-      dst[0] = v4u{packed[0], packed[1], packed[2], packed[3]};
-      dst[1] = v4u{packed[4], packed[5], packed[6], packed[7]};
-      x_scales[(size_t)g * M + row] = sb;
-    }
-
-    // ---- low-rank down-projection on bf16 MFMA
-    if constexpr (NTR > 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v4u a;
-        a.x = pack2_bf16(xh[8 * j + 0], xh[8 * j + 1]);
-        a.y = pack2_bf16(xh[8 * j + 2], xh[8 * j + 3]);
-        a.z = pack2_bf16(xh[8 * j + 4], xh[8 * j + 5]);
-        a.w = pack2_bf16(xh[8 * j + 6], xh[8 * j + 7]);
-        const v8bf av = __builtin_bit_cast(v8bf, a);
+    for (int b = 0; b < kActBatch; ++b) {
+      const int g = j0 + b * nwaves;
+      if (g >= G) break;  // uniform over the wave
+      const int k0 = g * kGroup + 16 * q;
+      const v4f* lp = reinterpret_cast<const v4f*>(inv_lambda + k0);
+      const v4f l0 = lp[0], l1 = lp[1], l2 = lp[2], l3 = lp[3];
+      v4u bfr[NTR > 0 ? NTR : 1][2];
+      if constexpr (NTR > 0) {
 #pragma unroll
         for (int t = 0; t < NTR; ++t) {
-          const v4u b = *reinterpret_cast<const v4u*>(L1 + (size_t)(t * 16 + rl) * K + k0 + 8 * j);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, b), acc[t], 0, 0, 0);
+          const v4u* bp = reinterpret_cast<const v4u*>(L1 + (size_t)(16 * t + rl) * K + k0);
+          bfr[t][0] = bp[0];
+          bfr[t][1] = bp[1];
+        }
+      }
+      float xh[16];
+      {
+        const v4u w0 = raw[b][0], w1 = raw[b][1];
+        xh[0] = __uint_as_float(w0.x << 16) * l0.x;
+        xh[1] = __uint_as_float(w0.x & 0xFFFF0000u) * l0.y;
+        xh[2] = __uint_as_float(w0.y << 16) * l0.z;
+        xh[3] = __uint_as_float(w0.y & 0xFFFF0000u) * l0.w;
+        xh[4] = __uint_as_float(w0.z << 16) * l1.x;
+        xh[5] = __uint_as_float(w0.z & 0xFFFF0000u) * l1.y;
+        xh[6] = __uint_as_float(w0.w << 16) * l1.z;
+        xh[7] = __uint_as_float(w0.w & 0xFFFF0000u) * l1.w;
+        xh[8] = __uint_as_float(w1.x << 16) * l2.x;
+        xh[9] = __uint_as_float(w1.x & 0xFFFF0000u) * l2.y;
+        xh[10] = __uint_as_float(w1.y << 16) * l2.z;
+        xh[11] = __uint_as_float(w1.y & 0xFFFF0000u) * l2.w;
+        xh[12] = __uint_as_float(w1.z << 16) * l3.x;
+        xh[13] = __uint_as_float(w1.z & 0xFFFF0000u) * l3.y;
+        xh[14] = __uint_as_float(w1.w << 16) * l3.z;
+        xh[15] = __uint_as_float(w1.w & 0xFFFF0000u) * l3.w;
+      }
+
+      // ---- group max over the row's four quarter lanes, scale, codes
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+      const uint16_t sb = int4_scale_bits(amax);
+      const float s = half_bits_to_float(sb);
+      const bool zero = s == 0.0f;
+      const float s1 = zero ? 1.0f : s;
+      const float rcp = 1.0f / s1;
+      float c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = __builtin_amdgcn_fmed3f(rne_quotient(xh[i], s1, rcp), -8.0f, 7.0f);
+        c[i] = zero ? 0.0f : v + 0.0f;  // + 0 turns a -0 code into +0
+      }
+      if (row < M) {
+        uint8_t* dst = xq + (size_t)row * ldq;
+        if constexpr (E3M2) {
+          *reinterpret_cast<v3u*>(dst + (size_t)g * 48 + 12 * q) = pack16_e3m2(c);
+        } else {
+          *reinterpret_cast<v2u*>(dst + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
+        }
+        if (q == 0) x_scales[(size_t)g * M + row] = sb;
+      }
+
+      // ---- low-rank down-projection on bf16 MFMA
+      if constexpr (NTR > 0) {
+        const v8bf a0 = to_bf16x8(xh), a1 = to_bf16x8(xh + 8);
+#pragma unroll
+        for (int t = 0; t < NTR; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, bfr[t][0]), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, bfr[t][1]), acc[t], 0, 0, 0);
         }
       }
     }
@@ -117,25 +153,19 @@ __global__ __launch_bounds__(512) void quantize_act_kernel(
   }
 }
 
-hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
-                               int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                               hipStream_t stream) {
+template <bool E3M2>
+static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                             int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
+                             hipStream_t stream) {
   const int G = K / kGroup;
-  const int nstrips = (G + 3) / 4;
-  // up to 8 waves; prefer a count that divides the strips evenly (12 strips -> 6 waves)
-  int nwaves = nstrips < 8 ? nstrips : 8;
-  for (int d = nwaves; d >= 4; --d)
-    if (nstrips % d == 0) {
-      nwaves = d;
-      break;
-    }
+  const int nwaves = G < kActMaxWaves ? G : kActMaxWaves;
   const size_t lds = (size_t)nwaves * 16 * r * sizeof(float);
-  dim3 grid((M + 15) / 16), block(64 * nwaves);
+  const dim3 grid((M + kActRows - 1) / kActRows), block(64 * nwaves);
   switch (r / 16) {
-#define SVDQ_ACT_CASE(n)                                                                  \
-  case n:                                                                                 \
-    hipLaunchKernelGGL(quantize_act_kernel<n>, grid, block, lds, stream, X, inv_lambda, L1, \
-                       M, K, xq, x_scales, T);                                            \
+#define SVDQ_ACT_CASE(n)                                                                   \
+  case n:                                                                                  \
+    hipLaunchKernelGGL((quantize_act_kernel<n, E3M2>), grid, block, lds, stream, X,         \
+                       inv_lambda, L1, M, K, xq, x_scales, T);                             \
     break;
     SVDQ_ACT_CASE(0)
     SVDQ_ACT_CASE(1)
@@ -151,6 +181,13 @@ hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                               int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
+                               int e3m2, hipStream_t stream) {
+  return e3m2 ? launch_act<true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream)
+              : launch_act<false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
 }
 
 }  // namespace svdq

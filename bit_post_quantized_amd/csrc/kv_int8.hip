@@ -36,8 +36,6 @@ constexpr int kKvWaves = 4;
 constexpr int kKvBatch = 16;                               // rows in flight per lane
 constexpr int kKvTokPerBlockQ = kKvWaves * kKvBatch;       // 64
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 
 // byte k of w as a float (selected to v_cvt_f32_ubyte{k})
 __device__ __forceinline__ float byte_to_float(uint32_t w, int k) {

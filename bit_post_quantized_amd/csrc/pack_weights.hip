@@ -1,15 +1,16 @@
-// Residual weight quantization and nibble packing (offline weight preparation).
+// Residual weight quantization and packing (offline weight preparation).
 //
 // Residual quantization of the SVD split (FLUX4 2.2 "three steps", third step) with the
 // symmetric b-bit rule of W4A8 3.1 at b = 4, per (64-group of k, output column n).
 // One thread owns one (g, n): it reads the 64 values R[g*64 .. g*64+63][n] (coalesced across
 // the threads of a row of R), finds the group max, derives the fp16 scale, codes the values
-// and writes 32 packed bytes to wq[n][g*32 ..] as two 16-byte stores.
+// and writes them to row n of wq as 32 bytes of nibbles or 48 bytes of BF6 (E3M2) codes.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
 namespace svdq {
 
+template <bool E3M2>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restrict__ R, int K,
                                                            int N, uint8_t* __restrict__ wq,
                                                            uint16_t* __restrict__ w_scales) {
@@ -26,18 +27,46 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
   }
   const uint16_t sb = int4_scale_bits(amax);
   const float s = half_bits_to_float(sb);
-  uint32_t packed[8];
-  quantize_group_int4(v, s, packed);
-  v4u* dst = reinterpret_cast<v4u*>(wq + (size_t)n * (K / 2) + (size_t)g * (kGroup / 2));
-  dst[0] = v4u{packed[0], packed[1], packed[2], packed[3]};
-  dst[1] = v4u{packed[4], packed[5], packed[6], packed[7]};
+  const bool zero = s == 0.0f;
+  const float s1 = zero ? 1.0f : s;
+  const float rcp = 1.0f / s1;
+  float c[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const float q = __builtin_amdgcn_fmed3f(rne_quotient(v[i], s1, rcp), -8.0f, 7.0f);
+    c[i] = zero ? 0.0f : q + 0.0f;  // + 0 turns a -0 code into +0
+  }
+  if constexpr (E3M2) {
+    uint32_t w[12];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v3u p = pack16_e3m2(c + 16 * j);
+      w[3 * j] = p.x;
+      w[3 * j + 1] = p.y;
+      w[3 * j + 2] = p.z;
+    }
+    v4u* dst = reinterpret_cast<v4u*>(wq + (size_t)n * (K / 4 * 3) + (size_t)g * 48);
+    dst[0] = v4u{w[0], w[1], w[2], w[3]};
+    dst[1] = v4u{w[4], w[5], w[6], w[7]};
+    dst[2] = v4u{w[8], w[9], w[10], w[11]};
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = pack8_nibbles(c + 8 * j);
+    v4u* dst = reinterpret_cast<v4u*>(wq + (size_t)n * (K / 2) + (size_t)g * (kGroup / 2));
+    dst[0] = v4u{w[0], w[1], w[2], w[3]};
+    dst[1] = v4u{w[4], w[5], w[6], w[7]};
+  }
   w_scales[(size_t)g * N + n] = sb;
 }
 
 hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
-                               hipStream_t stream) {
+                               int e3m2, hipStream_t stream) {
   dim3 grid((N + 255) / 256, K / kGroup);
-  hipLaunchKernelGGL(pack_weights_kernel, grid, dim3(256), 0, stream, R, K, N, wq, w_scales);
+  if (e3m2)
+    hipLaunchKernelGGL(pack_weights_kernel<true>, grid, dim3(256), 0, stream, R, K, N, wq, w_scales);
+  else
+    hipLaunchKernelGGL(pack_weights_kernel<false>, grid, dim3(256), 0, stream, R, K, N, wq, w_scales);
   return hipGetLastError();
 }
 

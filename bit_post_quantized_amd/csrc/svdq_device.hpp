@@ -17,6 +17,9 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 64;  // quantization group along K
 
@@ -68,28 +71,49 @@ __device__ __forceinline__ uint16_t int4_scale_bits(float amax) {
   return float_to_half_bits(amax / 7.0f);
 }
 
-// Codes of a whole 64-group, packed eight per dword (even k in the low nibble):
-// q = clamp(rne(fl32(x / s)), -8, 7), biased by 8, converted to bytes (v_cvt_pk_u8_f32),
-// merged pairwise into nibbles and un-biased by flipping bit 3 of every nibble.
-__device__ __forceinline__ void quantize_group_int4(const float* x, float s, uint32_t* packed) {
-  if (s == 0.0f) {
+// Eight codes (floats holding integers in [-8, 7]) -> one dword of nibbles, code i in bits
+// 4i .. 4i+3, two's complement: bias by 8, convert to bytes, merge even / odd, un-bias.
+__device__ __forceinline__ uint32_t pack8_nibbles(const float* c) {
+  uint32_t ev = 0u, od = 0u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) packed[j] = 0u;
-    return;
+  for (int e = 0; e < 4; ++e) {
+    ev = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * e] + 8.0f, e, ev);
+    od = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * e + 1] + 8.0f, e, od);
   }
-  const float rcp = 1.0f / s;
+  return ((od << 4) | ev) ^ 0x88888888u;
+}
+
+// ---------------------------------------------------------------- BF6 (E3M2) container
+// BF6 as defined by the OCP Microscaling format: sign bit 5, exponent bits 4..2 with bias 3,
+// mantissa bits 1..0.  An fp32 holding an integer code in [-8, 8] has at most two significant
+// mantissa bits after the leading one, so its E3M2 pattern is read straight out of the fp32
+// pattern: bits 30..21 hold (exponent + 127) << 2 | mantissa[22:21], and 127 - 3 = 124,
+// 124 << 2 = 496.  Both zeros map to +0.
+__device__ __forceinline__ uint32_t e3m2_of_code(float c) {
+  const uint32_t b = __float_as_uint(c);
+  const uint32_t p = (((b >> 21) & 0x3FFu) - 496u) | ((b >> 26) & 0x20u);
+  return (b << 1) == 0u ? 0u : p;
+}
+
+// Sixteen codes -> three dwords of the packed little-endian stream (code i at bits 6i..6i+5).
+__device__ __forceinline__ v3u pack16_e3m2(const float* c) {
+  uint32_t p[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t ev = 0u, od = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = rne_quotient(x[8 * j + 2 * e], s, rcp);
-      const float b = rne_quotient(x[8 * j + 2 * e + 1], s, rcp);
-      ev = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(a + 8.0f, 0.0f, 15.0f), e, ev);
-      od = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(b + 8.0f, 0.0f, 15.0f), e, od);
-    }
-    packed[j] = ((od << 4) | ev) ^ 0x88888888u;
-  }
+  for (int i = 0; i < 16; ++i) p[i] = e3m2_of_code(c[i]);
+  const uint32_t w0 = p[0] | (p[1] << 6) | (p[2] << 12) | (p[3] << 18) | (p[4] << 24) | (p[5] << 30);
+  const uint32_t w1 = (p[5] >> 2) | (p[6] << 4) | (p[7] << 10) | (p[8] << 16) | (p[9] << 22) | (p[10] << 28);
+  const uint32_t w2 = (p[10] >> 4) | (p[11] << 2) | (p[12] << 8) | (p[13] << 14) | (p[14] << 20) | (p[15] << 26);
+  return v3u{w0, w1, w2};
+}
+
+// Eight fp32 -> eight bf16 (round to nearest even, v_cvt_pk_bf16_f32) as an MFMA operand.
+__device__ __forceinline__ v8bf to_bf16x8(const float* x) {
+  v4u a;
+  a.x = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{x[0], x[1]}), v2bf));
+  a.y = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{x[2], x[3]}), v2bf));
+  a.z = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{x[4], x[5]}), v2bf));
+  a.w = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{x[6], x[7]}), v2bf));
+  return __builtin_bit_cast(v8bf, a);
 }
 
 // ---------------------------------------------------------------- nibble unpack

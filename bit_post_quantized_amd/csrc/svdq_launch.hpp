@@ -8,17 +8,23 @@
 
 namespace svdq {
 
+// e3m2 != 0: write the codes as BF6 (E3M2) records [rows, 3K/4] instead of nibbles [rows, K/2]
 hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
-                               hipStream_t stream);
+                               int e3m2, hipStream_t stream);
 
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                               hipStream_t stream);
+                               int e3m2, hipStream_t stream);
 
 hipError_t launch_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
                             const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
                             const uint16_t* bias, int M, int N, int K, int r, void* Y,
                             int out_fp32, int32_t* partials, hipStream_t stream);
+
+hipError_t launch_w4a4_gemm_e3m2(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                                 const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                                 const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                                 int out_fp32, int32_t* partials, hipStream_t stream);
 
 size_t kv_workspace_bytes(int tokens, int channels);
 

@@ -8,6 +8,8 @@ it is the offline preparation a toolbox performs once per checkpoint, not part o
 per-token path.
 
 Forward (device): ``svdq_quantize_act`` then ``svdq_w4a4_gemm``, two launches on one stream.
+With ``e3m2=True`` the codes travel as BF6 (E3M2) values and the ``*_e3m2`` entry points run
+the GEMM on the FP6 matrix units (same codes, scales and result; the faster path on gfx950).
 """
 from __future__ import annotations
 
@@ -27,13 +29,15 @@ class PackedWeights:
     inv_lambda: torch.Tensor  # fp32 [K]
     L1t: torch.Tensor         # bf16 [r, K]  (the [K, r] factor stored K-contiguous)
     L2t: torch.Tensor         # bf16 [N, r]  (the [r, N] factor stored r-contiguous)
-    wq: torch.Tensor          # uint8 [N, K/2]
+    wq: torch.Tensor          # uint8 [N, K/2] (nibbles) or [N, 3K/4] (BF6 codes)
     w_scales: torch.Tensor    # fp16 [K/64, N]
     bias: Optional[torch.Tensor] = None  # bf16 [N]
+    e3m2: bool = False        # container of wq (and of the activation codes in forward)
 
 
 def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
-                    bias: Optional[torch.Tensor] = None, device="cuda") -> PackedWeights:
+                    bias: Optional[torch.Tensor] = None, device="cuda",
+                    e3m2: bool = False) -> PackedWeights:
     """W bf16 [K, N] (Y = X W), X_calib bf16 [M, K] calibration activations."""
     K, N = W.shape
     Wd = W.detach().to("cpu", torch.float64)
@@ -56,14 +60,18 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
         L2b = torch.zeros(0, N, dtype=torch.bfloat16)
         R = W_hat
     R32 = R.to(torch.float32).to(device).contiguous()
-    wq = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
     w_scales = torch.empty(K // 64, N, dtype=torch.float16, device=device)
-    binding.svdq_pack_weights(R32, wq, w_scales)
+    if e3m2:
+        wq = torch.empty(N, K // 4 * 3, dtype=torch.uint8, device=device)
+        binding.svdq_pack_weights_e3m2(R32, wq, w_scales)
+    else:
+        wq = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
+        binding.svdq_pack_weights(R32, wq, w_scales)
     return PackedWeights(
         K=K, N=N, rank=rank, inv_lambda=inv32.to(device),
         L1t=L1b.t().contiguous().to(device), L2t=L2b.t().contiguous().to(device),
         wq=wq, w_scales=w_scales,
-        bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous())
+        bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2)
 
 
 @dataclass
@@ -73,9 +81,9 @@ class ActBuffers:
     T: Optional[torch.Tensor]
 
 
-def alloc_act(M: int, K: int, rank: int, device="cuda") -> ActBuffers:
+def alloc_act(M: int, K: int, rank: int, device="cuda", e3m2: bool = False) -> ActBuffers:
     return ActBuffers(
-        xq=torch.empty(M, K // 2, dtype=torch.uint8, device=device),
+        xq=torch.empty(M, K // 4 * 3 if e3m2 else K // 2, dtype=torch.uint8, device=device),
         x_scales=torch.empty(K // 64, M, dtype=torch.float16, device=device),
         T=torch.empty(M, rank, dtype=torch.float32, device=device) if rank > 0 else None)
 
@@ -86,11 +94,13 @@ def forward(X: torch.Tensor, pw: PackedWeights, out: Optional[torch.Tensor] = No
     """Y = SVDQuant-linear(X) for X bf16 [M, K] on the device."""
     M, K = X.shape
     if act is None:
-        act = alloc_act(M, K, pw.rank, X.device)
+        act = alloc_act(M, K, pw.rank, X.device, pw.e3m2)
     if out is None:
         out = torch.empty(M, pw.N, dtype=out_dtype, device=X.device)
-    binding.svdq_quantize_act(X, pw.inv_lambda, pw.L1t if pw.rank else None, pw.rank,
-                              act.xq, act.x_scales, act.T, stream)
-    binding.svdq_w4a4_gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales,
-                           pw.L2t if pw.rank else None, pw.bias, pw.rank, out, stream)
+    quantize = binding.svdq_quantize_act_e3m2 if pw.e3m2 else binding.svdq_quantize_act
+    gemm = binding.svdq_w4a4_gemm_e3m2 if pw.e3m2 else binding.svdq_w4a4_gemm
+    quantize(X, pw.inv_lambda, pw.L1t if pw.rank else None, pw.rank, act.xq, act.x_scales,
+             act.T, stream)
+    gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales, pw.L2t if pw.rank else None,
+         pw.bias, pw.rank, out, stream)
     return out

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 1
+#define SVDQ_ABI_VERSION 2
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -116,6 +116,37 @@ int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
  */
 int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int32_t* P,
                        void* stream);
+
+/*
+ * BF6 (E3M2) container.  The *_e3m2 entry points compute exactly the same codes, scales, T and
+ * Y as the entry points above; only the byte layout of the codes differs.  Each code is stored
+ * as its 6-bit BF6 pattern (OCP Microscaling format E3M2: sign bit 5, exponent bits 4..2 with
+ * bias 3, mantissa bits 1..0; every integer in [-8, 8] is exact), and a row of K codes is one
+ * little-endian bit stream of 3K/4 bytes in which code k occupies bits 6k .. 6k+5, so 64-group
+ * g is the 48-byte record at byte 48 g.  The FP6 matrix units of gfx950 read this container
+ * directly (FLUX4 3.2: a small float format on the matrix units avoids the 4-bit unpack),
+ * which is why the GEMM that consumes it is the fast path.
+ *
+ * svdq_pack_weights_e3m2 — svdq_pack_weights with
+ *   wq6       uint8 [N, 3K/4]                                              16B
+ * svdq_quantize_act_e3m2 — svdq_quantize_act with
+ *   xq6       uint8 [M, 3K/4]                                              16B
+ * svdq_w4a4_gemm_e3m2 — svdq_w4a4_gemm reading xq6 / wq6 (same Y up to fp32 summation order).
+ * svdq_w4a4_partials_e3m2 — test entry: the exact group partials of the same device inner loop
+ *   as svdq_w4a4_gemm_e3m2, P int32 [G, M, N].
+ * Arguments, shapes, alignment and error behaviour are those of the matching entry point above.
+ */
+int svdq_pack_weights_e3m2(const float* R, int K, int N, uint8_t* wq6, uint16_t* w_scales,
+                           void* stream);
+int svdq_quantize_act_e3m2(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                           int M, int K, int r, uint8_t* xq6, uint16_t* x_scales, float* T,
+                           void* stream);
+int svdq_w4a4_gemm_e3m2(const uint8_t* xq6, const uint16_t* x_scales, const float* T,
+                        const uint8_t* wq6, const uint16_t* w_scales, const uint16_t* L2,
+                        const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                        int out_dtype, void* stream);
+int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N, int K,
+                            int32_t* P, void* stream);
 
 /*
  * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its

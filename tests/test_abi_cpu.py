@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 1
+    assert lib.svdq_abi_version() == 2
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -78,6 +78,25 @@ def test_gemm_validation(lib):
     assert g(*args, 8, 8, 128, 0, ODD, 0, None) == binding.SVDQ_EALIGN
     assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK
     p = lib.svdq_w4a4_partials
+    assert p(FAKE, FAKE, 8, 8, 96, FAKE, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
+
+
+def test_e3m2_entry_points_validate_like_their_nibble_twins(lib):
+    assert lib.svdq_pack_weights_e3m2(FAKE, 100, 8, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert lib.svdq_pack_weights_e3m2(ODD, 64, 8, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    assert b"svdq_pack_weights_e3m2" not in lib.svdq_last_error()  # validation message, not HIP
+    f = lib.svdq_quantize_act_e3m2
+    assert f(FAKE, FAKE, FAKE, 4, 128, 20, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, None, 4, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, FAKE, FAKE, 0, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_OK
+    g = lib.svdq_w4a4_gemm_e3m2
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert g(*args, 8, 8, 100, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert g(*args, 8, 8, 128, 0, FAKE, 7, None) == binding.SVDQ_EINVAL
+    assert g(*args, 8, 8, 128, 0, ODD, 0, None) == binding.SVDQ_EALIGN
+    assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK
+    p = lib.svdq_w4a4_partials_e3m2
     assert p(FAKE, FAKE, 8, 8, 96, FAKE, None) == binding.SVDQ_ESHAPE
     assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
 
