@@ -31,6 +31,7 @@ _SIGNATURES = {
     "svdq_quantize_act": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "svdq_w4a4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "svdq_w4a4_partials": ([_P, _P, _I, _I, _I, _P, _P], _I),
+    "svdq_e3m2_bytes": ([_I, _I], ctypes.c_size_t),
     "svdq_pack_weights_e3m2": ([_P, _I, _I, _P, _P, _P], _I),
     "svdq_quantize_act_e3m2": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "svdq_w4a4_gemm_e3m2": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
@@ -132,9 +133,14 @@ def svdq_w4a4_partials(xq: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
         _ptr(xq), _ptr(wq), M, N, 2 * half_k, _ptr(P), _stream(stream)))
 
 
+def svdq_e3m2_bytes(rows: int, K: int) -> int:
+    """Bytes of the tiled BF6 code container of a [rows, K] code matrix."""
+    return load().svdq_e3m2_bytes(rows, K)
+
+
 def svdq_pack_weights_e3m2(R: torch.Tensor, wq6: torch.Tensor, w_scales: torch.Tensor,
                            stream=None) -> None:
-    """R fp32 [K, N] -> wq6 uint8 [N, 3K/4] (BF6 codes), w_scales fp16 [K/64, N]."""
+    """R fp32 [K, N] -> wq6 (tiled BF6 container, svdq_e3m2_bytes(N, K) bytes), w_scales."""
     K, N = R.shape
     _check("svdq_pack_weights_e3m2", load().svdq_pack_weights_e3m2(
         _ptr(R), K, N, _ptr(wq6), _ptr(w_scales), _stream(stream)))
@@ -144,39 +150,32 @@ def svdq_quantize_act_e3m2(X: torch.Tensor, inv_lambda: torch.Tensor,
                            L1: Optional[torch.Tensor], r: int, xq6: torch.Tensor,
                            x_scales: torch.Tensor, T: Optional[torch.Tensor],
                            stream=None) -> None:
-    """As svdq_quantize_act with the codes written as BF6: xq6 uint8 [M, 3K/4]."""
+    """As svdq_quantize_act with the codes written to xq6, the tiled BF6 container of M rows."""
     M, K = X.shape
     _check("svdq_quantize_act_e3m2", load().svdq_quantize_act_e3m2(
         _ptr(X), _ptr(inv_lambda), _ptr(L1), M, K, r, _ptr(xq6), _ptr(x_scales), _ptr(T),
         _stream(stream)))
 
 
-def _k_of_e3m2(cols: int) -> int:
-    if cols % 3:
-        raise ValueError("a BF6 code row has 3K/4 bytes")
-    return cols // 3 * 4
-
-
 def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
                         wq6: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
                         bias: Optional[torch.Tensor], r: int, Y: torch.Tensor,
                         stream=None) -> None:
-    """As svdq_w4a4_gemm, reading BF6 codes (xq6 [M, 3K/4], wq6 [N, 3K/4])."""
-    M, cols = xq6.shape
-    N = wq6.shape[0]
+    """As svdq_w4a4_gemm, reading the BF6 containers (M, N, K from x_scales [K/64, M] and
+    w_scales [K/64, N])."""
+    G, M = x_scales.shape
+    N = w_scales.shape[1]
     out = SVDQ_OUT_FP32 if Y.dtype == torch.float32 else SVDQ_OUT_BF16
     _check("svdq_w4a4_gemm_e3m2", load().svdq_w4a4_gemm_e3m2(
         _ptr(xq6), _ptr(x_scales), _ptr(T), _ptr(wq6), _ptr(w_scales), _ptr(L2), _ptr(bias),
-        M, N, _k_of_e3m2(cols), r, _ptr(Y), out, _stream(stream)))
+        M, N, 64 * G, r, _ptr(Y), out, _stream(stream)))
 
 
-def svdq_w4a4_partials_e3m2(xq6: torch.Tensor, wq6: torch.Tensor, P: torch.Tensor,
-                            stream=None) -> None:
+def svdq_w4a4_partials_e3m2(xq6: torch.Tensor, wq6: torch.Tensor, M: int, N: int, K: int,
+                            P: torch.Tensor, stream=None) -> None:
     """P int32 [K/64, M, N]: the exact group partials of the BF6 GEMM's inner loop."""
-    M, cols = xq6.shape
-    N = wq6.shape[0]
     _check("svdq_w4a4_partials_e3m2", load().svdq_w4a4_partials_e3m2(
-        _ptr(xq6), _ptr(wq6), M, N, _k_of_e3m2(cols), _ptr(P), _stream(stream)))
+        _ptr(xq6), _ptr(wq6), M, N, K, _ptr(P), _stream(stream)))
 
 
 def kv_int8_workspace_bytes(tokens: int, channels: int) -> int:

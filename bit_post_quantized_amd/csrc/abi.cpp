@@ -176,6 +176,11 @@ int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
               bias, M, N, K, r, Y, out_dtype, stream);
 }
 
+size_t svdq_e3m2_bytes(int rows, int K) {
+  if (rows <= 0 || K <= 0 || K % 64 != 0) return 0;
+  return (size_t)((rows + 31) / 32) * (size_t)(K / 64) * (64 * 24);
+}
+
 int svdq_w4a4_gemm_e3m2(const uint8_t* xq6, const uint16_t* x_scales, const float* T,
                         const uint8_t* wq6, const uint16_t* w_scales, const uint16_t* L2,
                         const uint16_t* bias, int M, int N, int K, int r, void* Y,

@@ -12,8 +12,11 @@
 // 16 rows x 64 contiguous bytes.  The loads of kActBatch groups are issued before any of them is
 // used.  The group max is folded over the four quarter lanes of a row with two lane shuffles;
 // every lane then codes its 16 values (exact quotient, no division per element) and writes
-// them as 8 bytes of nibbles or 12 bytes of BF6 (E3M2) codes -- the two containers the GEMMs
-// read -- and the quarter-0 lanes write the 16 rows' scales (32 contiguous bytes).
+// them as 8 bytes of nibbles, or as 12 bytes of BF6 (E3M2) codes into the tiled container (its
+// row block, group, slot row % 32 + 32 (q / 2), byte 12 (q % 2)) -- the two containers the GEMMs
+// read -- and the quarter-0 lanes write the 16 rows' scales (32 contiguous bytes).  For the
+// tiled container the grid also covers the rows up to the next multiple of 32, whose codes it
+// writes as zeros.
 // Low-rank branch: the same registers rounded to bf16 are the A operand of two
 // v_mfma_f32_16x16x32_bf16 per group (k-slots 8 (l / 16) + i of the MFMA take k = 16 q + i and
 // 16 q + 8 + i), and L1, stored K-contiguous, is loaded with the same k map, so the MFMAs sum
@@ -45,7 +48,6 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
   const int row_ld = row < M ? row : M - 1;
   const int G = K / kGroup;
   const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
-  const size_t ldq = E3M2 ? (size_t)K / 4 * 3 : (size_t)K / 2;
 
   v4f acc[NTR > 0 ? NTR : 1];
 #pragma unroll
@@ -108,19 +110,20 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
       const bool zero = s == 0.0f;
       const float s1 = zero ? 1.0f : s;
       const float rcp = 1.0f / s1;
+      const bool live = row < M;
       float c[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float v = __builtin_amdgcn_fmed3f(rne_quotient(xh[i], s1, rcp), -8.0f, 7.0f);
-        c[i] = zero ? 0.0f : v + 0.0f;  // + 0 turns a -0 code into +0
+        c[i] = (zero || !live) ? 0.0f : v + 0.0f;  // + 0 turns a -0 code into +0
       }
-      if (row < M) {
-        uint8_t* dst = xq + (size_t)row * ldq;
-        if constexpr (E3M2) {
-          *reinterpret_cast<v3u*>(dst + (size_t)g * 48 + 12 * q) = pack16_e3m2(c);
-        } else {
-          *reinterpret_cast<v2u*>(dst + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
-        }
+      if constexpr (E3M2) {  // rows up to the block boundary (padding rows get zero codes)
+        uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
+        *reinterpret_cast<v3u*>(dst) = pack16_e3m2(c);
+      }
+      if (live) {
+        if constexpr (!E3M2)
+          *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
         if (q == 0) x_scales[(size_t)g * M + row] = sb;
       }
 
@@ -160,7 +163,9 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
   const int G = K / kGroup;
   const int nwaves = G < kActMaxWaves ? G : kActMaxWaves;
   const size_t lds = (size_t)nwaves * 16 * r * sizeof(float);
-  const dim3 grid((M + kActRows - 1) / kActRows), block(64 * nwaves);
+  // the tiled BF6 container is written up to the next multiple of 32 rows
+  const int rows = E3M2 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
+  const dim3 grid((rows + kActRows - 1) / kActRows), block(64 * nwaves);
   switch (r / 16) {
 #define SVDQ_ACT_CASE(n)                                                                   \
   case n:                                                                                  \

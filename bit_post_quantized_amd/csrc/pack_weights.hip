@@ -4,7 +4,9 @@
 // symmetric b-bit rule of W4A8 3.1 at b = 4, per (64-group of k, output column n).
 // One thread owns one (g, n): it reads the 64 values R[g*64 .. g*64+63][n] (coalesced across
 // the threads of a row of R), finds the group max, derives the fp16 scale, codes the values
-// and writes them to row n of wq as 32 bytes of nibbles or 48 bytes of BF6 (E3M2) codes.
+// and writes them to row n of wq as 32 bytes of nibbles, or as two 24-byte slots of the tiled
+// BF6 (E3M2) container (block n / 32, group g, slots n % 32 and 32 + n % 32).  For the tiled
+// container the grid covers columns up to the next multiple of 32 and writes zero codes there.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
@@ -16,13 +18,15 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
                                                            uint16_t* __restrict__ w_scales) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   const int g = blockIdx.y;
-  if (n >= N) return;
-  const float* col = R + (size_t)g * kGroup * N + n;
+  const int n_end = E3M2 ? (N + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : N;
+  if (n >= n_end) return;
+  const bool live = n < N;
+  const float* col = R + (size_t)g * kGroup * N + (live ? n : 0);
   float v[kGroup];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
-    v[i] = col[(size_t)i * N];
+    v[i] = live ? col[(size_t)i * N] : 0.0f;
     amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
   }
   const uint16_t sb = int4_scale_bits(amax);
@@ -45,10 +49,15 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
       w[3 * j + 1] = p.y;
       w[3 * j + 2] = p.z;
     }
-    v4u* dst = reinterpret_cast<v4u*>(wq + (size_t)n * (K / 4 * 3) + (size_t)g * 48);
-    dst[0] = v4u{w[0], w[1], w[2], w[3]};
-    dst[1] = v4u{w[4], w[5], w[6], w[7]};
-    dst[2] = v4u{w[8], w[9], w[10], w[11]};
+    uint8_t* blk = wq + ((size_t)(n >> 5) * (K / kGroup) + g) * kE3m2Block;
+    v2u* s0 = reinterpret_cast<v2u*>(blk + (n & 31) * 24);         // codes k = 0..31
+    v2u* s1 = reinterpret_cast<v2u*>(blk + (32 + (n & 31)) * 24);  // codes k = 32..63
+    s0[0] = v2u{w[0], w[1]};
+    s0[1] = v2u{w[2], w[3]};
+    s0[2] = v2u{w[4], w[5]};
+    s1[0] = v2u{w[6], w[7]};
+    s1[1] = v2u{w[8], w[9]};
+    s1[2] = v2u{w[10], w[11]};
   } else {
     uint32_t w[8];
 #pragma unroll
@@ -57,12 +66,13 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const float* __restri
     dst[0] = v4u{w[0], w[1], w[2], w[3]};
     dst[1] = v4u{w[4], w[5], w[6], w[7]};
   }
-  w_scales[(size_t)g * N + n] = sb;
+  if (live) w_scales[(size_t)g * N + n] = sb;
 }
 
 hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
                                int e3m2, hipStream_t stream) {
-  dim3 grid((N + 255) / 256, K / kGroup);
+  const int cols = e3m2 ? (N + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : N;
+  dim3 grid((cols + 255) / 256, K / kGroup);
   if (e3m2)
     hipLaunchKernelGGL(pack_weights_kernel<true>, grid, dim3(256), 0, stream, R, K, N, wq, w_scales);
   else

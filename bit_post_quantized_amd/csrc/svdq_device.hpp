@@ -95,6 +95,13 @@ __device__ __forceinline__ uint32_t e3m2_of_code(float c) {
   return (b << 1) == 0u ? 0u : p;
 }
 
+// Tiled BF6 container of a [R, K] code matrix: ceil(R / 32) row blocks; block b holds, group by
+// group, 64 slots of 24 bytes; slot s carries the 32 codes of row 32 b + s % 32 at
+// k = 64 g + 32 (s / 32) + i as one 192-bit stream -- the lane order of the 32 x 32 x 64 FP6
+// MFMA operand, so a GEMM stage is a plain copy of whole blocks.
+constexpr int kE3m2Rows = 32;
+constexpr int kE3m2Block = 64 * 24;  // one row block x one group
+
 // Sixteen codes -> three dwords of the packed little-endian stream (code i at bits 6i..6i+5).
 __device__ __forceinline__ v3u pack16_e3m2(const float* c) {
   uint32_t p[16];

@@ -14,18 +14,18 @@
 // gfx950 mapping (one workgroup = 4 waves = a 128 x 128 tile of Y; wave (wm, wn) owns the
 // 64 x 64 sub-tile made of 2 x 2 tiles of 32 x 32):
 //  * MFMA operand layout (32 x 32 x 64 f8f6f4, BF6): lane l supplies row (or column) l % 32 and
-//    the 32 codes k = 32 (l / 32) + i as six dwords, code i at bits 6i .. 6i+5 -- exactly half
-//    of a group's 48-byte record in the packed stream.  The 32 x 32 result: lane l holds column
-//    l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..15.
-//  * Staging.  KS = 2 groups per stage.  Thread t copies the two 24-byte halves of one
-//    (row, group) record (three 16-byte global loads) into "lane slots": for every 32-row tile
-//    and group, 64 consecutive 24-byte slots in MFMA lane order, so a fragment is three
-//    conflict-free ds_read_b64 per lane.  Two LDS buffers alternate; the next stage's global
-//    loads are in flight while the current one is computed; one barrier per stage.
+//    the 32 codes k = 32 (l / 32) + i as six dwords, code i at bits 6i .. 6i+5 -- exactly slot
+//    l of a (row block, group) block of the tiled container.  The 32 x 32 result: lane l holds
+//    column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..15.
+//  * Staging.  KS = 2 groups per stage, NB = 3 stages resident in LDS, two of them in flight:
+//    codes and scales go from global memory straight into LDS (global_load_lds, 16-byte and
+//    2-byte), so no registers or VALU work are spent on staging and the loads of stage s + 2
+//    are issued while stage s is computed.  The tiled container's blocks are copied as they
+//    are, so an MFMA operand is three ds_read_b64 per lane from its 24-byte slot.
 //  * Scale products.  s_x[m] * s_w[n] for a 32 x 32 tile is an outer product that
-//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) when only k-slot 0
-//    is nonzero: the scales sit in LDS slots 0..31 and slots 32..63 hold zeros, so every lane's
-//    operand is one ds_read_u16.  The dequantization is one FMA per output and group.
+//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) from fp16 pairs
+//    read straight from LDS (see the operand note in the kernel); the factor 2 it carries is
+//    removed once at the end.  The dequantization is one FMA per output and group.
 //  * Epilogue.  bf16(T) [32 x 16] and L2 [16 x 32] fragments go through
 //    v_mfma_f32_32x32x16_bf16 with the fp32 accumulator as C, then the bias is added and the
 //    tile is rounded to bf16 (or kept fp32) and stored.
@@ -39,23 +39,30 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 namespace f6 {
-constexpr int kRecord = 48;                         // one 64-group of one row: 64 x 6 bits
-constexpr int kSlot = 24;                           // one lane's half of a record
-constexpr int kBlock = 64 * kSlot + 16;             // 64 lane slots (+16 bytes against bank aliasing)
-constexpr int TM = 128, TN = 128;                   // workgroup tile
-constexpr int KS = 2;                               // groups per LDS stage
-constexpr int THREADS = 256;                        // 2 x 2 waves of 64 x 64
-constexpr int RT = TM / 32, CT = TN / 32;           // 32 x 32 tiles along M and N
-constexpr int kOpA = RT * KS * kBlock;
-constexpr int kOpB = CT * KS * kBlock;
-constexpr int kScA = KS * RT * 64 * 2;              // fp16 [KS][RT][64 slots]
-constexpr int kScB = KS * CT * 64 * 2;
-constexpr int kStage = kOpA + kOpB + kScA + kScB;
-constexpr int kLds = 2 * kStage;
-static_assert(TM * KS == THREADS && TN * KS == THREADS, "one record per thread and operand");
+constexpr int TM = 128, TN = 128;             // workgroup tile
+constexpr int KS = 2;                         // groups per stage
+constexpr int NB = 3;                         // stages resident in LDS (two in flight)
+constexpr int THREADS = 256;                  // 2 x 2 waves of 64 x 64
+constexpr int RT = TM / 32, CT = TN / 32;     // 32 x 32 tiles along M and N
+constexpr int kFrag = kE3m2Block;             // one 32-row block x one group, 64 lane slots
+constexpr int kOpA = RT * KS * kFrag;         // [tile][group][64 slots][24 B]
+constexpr int kOpB = CT * KS * kFrag;
+constexpr int kScA = KS * TM * 4;             // [group][row], one zero-extended fp16 per dword
+constexpr int kScB = KS * TN * 4;
+constexpr int kStage = kScA + kScB + kOpA + kOpB;  // s_x, s_w, A, B
+constexpr int kLds = NB * kStage;
+constexpr int kLoadsA = kOpA / 16 / THREADS;  // 16-byte direct-to-LDS loads per thread and stage
+constexpr int kLoadsB = kOpB / 16 / THREADS;
+static_assert(kLoadsA * 16 * THREADS == kOpA && kLoadsB * 16 * THREADS == kOpB, "load split");
 static_assert(KS * TM == THREADS && KS * TN == THREADS, "one scale per thread and operand");
-static_assert(kBlock % 16 == 0 && kStage % 16 == 0, "16-byte aligned LDS areas");
+static_assert(kStage % 16 == 0, "16-byte aligned stages");
 }  // namespace f6
+
+#define SVDQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding: vmcnt in bits 3..0
+// and 15..14, expcnt 6..4, lgkmcnt 11..8)
+#define SVDQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 template <bool OUT_FP32, bool PARTIALS, int NTR>
 __global__ __launch_bounds__(f6::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
@@ -68,76 +75,90 @@ void w4a4_gemm_e3m2_kernel(
   using namespace f6;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int r = 16 * NTR;
+  constexpr int kLoads = kLoadsA + kLoadsB + (PARTIALS ? 0 : 2);  // per thread and stage
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to SGPRs
   const int wm = wave >> 1, wn = wave & 1;
   const int m_tile = blockIdx.y * TM, n_tile = blockIdx.x * TN;
+
+  // ---- direct-to-LDS staging.  The codes arrive in the tiled container, whose (row block,
+  //      group) blocks are exactly the MFMA operand blocks, so a stage is a copy of
+  //      KS consecutive blocks per 32-row tile into LDS ([tile][group][64 slots][24 B]).  Load j
+  //      of thread t moves 16-byte chunk c = j * 256 + t of the stage (each load instruction of
+  //      a wave fills 1 KB of consecutive LDS, lane l at +16 l): byte 16 (c % 96) of the block
+  //      (tile (c / 96) / KS, group (c / 96) % KS) -- a fixed per-lane pointer plus the stage's
+  //      uniform group offset.  Tiles past the last row block re-read that block (unused rows).
   const int G = K / kGroup;
-  const size_t ldq = (size_t)K / 4 * 3;
-
-  // ---- staging map: thread t moves record (row t / KS, group t % KS) of A and of B, and the
-  //      scale of (group t / TM, row t % TM) of s_x and of (group t / TN, column t % TN) of s_w
-  const int u_row = tid / KS, u_g = tid % KS;
-  const uint8_t* a_src = xq + (size_t)min(m_tile + u_row, M - 1) * ldq;
-  const uint8_t* b_src = wq + (size_t)min(n_tile + u_row, N - 1) * ldq;
-  const int a_dst = ((u_row >> 5) * KS + u_g) * kBlock + (u_row & 31) * kSlot;
-  const int b_dst = kOpA + a_dst;
-  const int s_g = tid / TM, s_r = tid % TM;
-  const uint16_t* sx_src = PARTIALS ? nullptr : x_scales + min(m_tile + s_r, M - 1);
-  const uint16_t* sw_src = PARTIALS ? nullptr : w_scales + min(n_tile + s_r, N - 1);
-  const int sx_dst = kOpA + kOpB + (s_g * RT + (s_r >> 5)) * 128 + (s_r & 31) * 2;
-  const int sw_dst = kOpA + kOpB + kScA + (s_g * CT + (s_r >> 5)) * 128 + (s_r & 31) * 2;
-
-  struct Regs {
-    v4u a[3], b[3];
-    uint32_t sx, sw;
-  };
-  auto load_stage = [&](int s, Regs& R) {
-    const int g = min(s * KS + u_g, G - 1);
-    const v4u* pa = reinterpret_cast<const v4u*>(a_src + (size_t)g * kRecord);
-    const v4u* pb = reinterpret_cast<const v4u*>(b_src + (size_t)g * kRecord);
+  const int mblk = (M + 31) / 32, nblk = (N + 31) / 32;
+  const uint8_t* a_ptr[kLoadsA];
+  const uint8_t* b_ptr[kLoadsB];
+  int a_g[kLoadsA];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      R.a[c] = pa[c];
-      R.b[c] = pb[c];
-    }
-    if constexpr (!PARTIALS) {
-      const int gs = s * KS + s_g;
-      const int gl = min(gs, G - 1);
-      const uint32_t keep = gs < G ? 0xFFFFu : 0u;  // a group past the end gets zero scales
-      R.sx = sx_src[(size_t)gl * M] & keep;
-      R.sw = sw_src[(size_t)gl * N] & keep;
-    }
-  };
-  auto store_stage = [&](int buf, const Regs& R) {
-    uint8_t* st = lds + buf * kStage;
-    v2u* a0 = reinterpret_cast<v2u*>(st + a_dst);
-    v2u* a1 = reinterpret_cast<v2u*>(st + a_dst + 32 * kSlot);
-    a0[0] = v2u{R.a[0].x, R.a[0].y};
-    a0[1] = v2u{R.a[0].z, R.a[0].w};
-    a0[2] = v2u{R.a[1].x, R.a[1].y};
-    a1[0] = v2u{R.a[1].z, R.a[1].w};
-    a1[1] = v2u{R.a[2].x, R.a[2].y};
-    a1[2] = v2u{R.a[2].z, R.a[2].w};
-    v2u* b0 = reinterpret_cast<v2u*>(st + b_dst);
-    v2u* b1 = reinterpret_cast<v2u*>(st + b_dst + 32 * kSlot);
-    b0[0] = v2u{R.b[0].x, R.b[0].y};
-    b0[1] = v2u{R.b[0].z, R.b[0].w};
-    b0[2] = v2u{R.b[1].x, R.b[1].y};
-    b1[0] = v2u{R.b[1].z, R.b[1].w};
-    b1[1] = v2u{R.b[2].x, R.b[2].y};
-    b1[2] = v2u{R.b[2].z, R.b[2].w};
-    if constexpr (!PARTIALS) {
-      *reinterpret_cast<uint16_t*>(st + sx_dst) = (uint16_t)R.sx;
-      *reinterpret_cast<uint16_t*>(st + sw_dst) = (uint16_t)R.sw;
+  for (int j = 0; j < kLoadsA; ++j) {
+    const int c = j * THREADS + tid, blk = c / 96;
+    const int tile = blk / KS;
+    a_g[j] = blk % KS;
+    const size_t within = (size_t)a_g[j] * kFrag + (c % 96) * 16;
+    a_ptr[j] = xq + (size_t)min(m_tile / 32 + tile, mblk - 1) * G * kFrag + within;
+    b_ptr[j] = wq + (size_t)min(n_tile / 32 + tile, nblk - 1) * G * kFrag + within;
+  }
+  // scales: thread t loads s_x of (group t / TM, row t % TM) and s_w of (group t / TN,
+  // column t % TN) as 2-byte direct loads, which land zero-extended in dword t of the area;
+  // the group of a scale load is uniform over the wave
+  const int s_gq = wave >> 1;
+  const uint16_t* sx_ptr = PARTIALS ? nullptr : x_scales + (size_t)s_gq * M + min(m_tile + tid % TM, M - 1);
+  const uint16_t* sw_ptr = PARTIALS ? nullptr : w_scales + (size_t)s_gq * N + min(n_tile + tid % TN, N - 1);
+
+  auto issue_stage = [&](int s) {
+    uint8_t* st = lds + (s % NB) * kStage;
+    const int g0 = s * KS;
+    if (g0 + KS <= G) {  // every stage but the last one of an odd G
+      if constexpr (!PARTIALS) {
+        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g0 * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
+        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g0 * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
+      }
+      const size_t go = (size_t)g0 * kFrag;
+#pragma unroll
+      for (int j = 0; j < kLoadsA; ++j) {
+        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
+      }
+    } else {  // groups past the end re-read group G - 1 (loaded, never used)
+      if constexpr (!PARTIALS) {
+        const int g = min(g0 + s_gq, G - 1) - s_gq;
+        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
+        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kLoadsA; ++j) {
+        const size_t go = (size_t)(min(g0 + a_g[j], G - 1) - a_g[j]) * kFrag;
+        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
+      }
     }
   };
 
-  // ---- per-lane fragment offsets inside a stage
-  const int a_frag = (2 * wm * KS) * kBlock + lane * kSlot;       // + (i * KS + gg) * kBlock
-  const int b_frag = kOpA + (2 * wn * KS) * kBlock + lane * kSlot;
-  const int sa_frag = kOpA + kOpB + (2 * wm) * 128 + lane * 2;     // + (gg * RT + i) * 128
-  const int sb_frag = kOpA + kOpB + kScA + (2 * wn) * 128 + lane * 2;
+  // ---- per-lane read offsets inside a stage.  MFMA operand of 32-row tile i, group gg: lane
+  //      l reads its 24-byte slot at +0, +8, +16 (consecutive lanes 24 bytes apart: the 16
+  //      lanes of a read phase hit 32 distinct banks).
+  // One base register per 32-row tile (kept opaque): the three reads of an operand then merge
+  // into one ds_read2_b64 + one ds_read_b64 that land in the operand's registers, instead of
+  // being paired with the same read of the other tile.
+  int a_base[2], b_base[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    a_base[i] = kScA + kScB + ((2 * wm + i) * KS) * kFrag + lane * 24;
+    b_base[i] = kScA + kScB + kOpA + ((2 * wn + i) * KS) * kFrag + lane * 24;
+    asm volatile("" : "+v"(a_base[i]), "+v"(b_base[i]));
+  }
+  // scale-product operands (v_mfma_f32_32x32x8_f16, fp16 pairs): A gets the dwords of rows
+  // r and r + 1 -- (s_x[r], 0, s_x[r+1], 0) -- and B gets (s_w[n], 0, 0, 0) from its dword and
+  // a zero, so the product of k-slot pairs is s_x[r] s_w[n] + s_x[r+1] * 0; both lane
+  // halves hold the same values, so the MFMA returns exactly 2 s_x s_w.  (Row r + 1 of the
+  // last s_x entry is the first s_w entry: a finite fp16 value times zero.)
+  const int sa_off = (32 * 2 * wm + (lane & 31)) * 4;            // + (gg * TM + 32 i) * 4
+  const int sb_off = kScA + (32 * 2 * wn + (lane & 31)) * 4;    // + (gg * TN + 32 j) * 4
 
   v16f acc[2][2];
 #pragma unroll
@@ -148,44 +169,65 @@ void w4a4_gemm_e3m2_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   const v16f zero16 = acc[0][0];
 
-  // scale slots 32..63 of both buffers must read as zero; the staging never writes them
-  if constexpr (!PARTIALS) {
-    for (int o = tid * 16; o < kScA + kScB; o += THREADS * 16) {
-      *reinterpret_cast<v4u*>(lds + kOpA + kOpB + o) = v4u{0u, 0u, 0u, 0u};
-      *reinterpret_cast<v4u*>(lds + kStage + kOpA + kOpB + o) = v4u{0u, 0u, 0u, 0u};
-    }
-  }
   const int S = (G + KS - 1) / KS;
-  Regs R;
-  load_stage(0, R);
-  __syncthreads();
-  store_stage(0, R);
-  __syncthreads();
+  issue_stage(0);
+  if (S > 1) issue_stage(1);
 
-  for (int s = 0; s < S; ++s) {
-    if (s + 1 < S) load_stage(s + 1, R);
-    const uint8_t* st = lds + (s & 1) * kStage;
-    const int ng = min(KS, G - s * KS);
+  // one group's MFMA operands, read from LDS
+  struct Frag {
+    v8i A[2], B[2];
+    v4h SA[2], SB[2];
+  };
+  auto read_frag = [&](const uint8_t* st, int gg, Frag& F) {
 #pragma unroll
-    for (int gg = 0; gg < KS; ++gg) {
-      if (gg >= ng) break;  // uniform
-      v8i A[2], B[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const v2u* pa = reinterpret_cast<const v2u*>(st + a_frag + (i * KS + gg) * kBlock);
-        const v2u* pb = reinterpret_cast<const v2u*>(st + b_frag + (i * KS + gg) * kBlock);
-        const v2u a0 = pa[0], a1 = pa[1], a2 = pa[2];
-        const v2u b0 = pb[0], b1 = pb[1], b2 = pb[2];
-        A[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
-        B[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, 0, 0};
+    for (int i = 0; i < 2; ++i) {
+      const v2u* pa = reinterpret_cast<const v2u*>(st + a_base[i] + gg * kFrag);
+      const v2u* pb = reinterpret_cast<const v2u*>(st + b_base[i] + gg * kFrag);
+      const v2u a0 = pa[0], a1 = pa[1], a2 = pa[2];
+      const v2u b0 = pb[0], b1 = pb[1], b2 = pb[2];
+      F.A[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
+      F.B[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, 0, 0};
+      if constexpr (!PARTIALS) {
+        const v2u sx = *reinterpret_cast<const v2u*>(st + sa_off + (gg * TM + 32 * i) * 4);
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + sb_off + (gg * TN + 32 * i) * 4);
+        F.SA[i] = __builtin_bit_cast(v4h, sx);
+        F.SB[i] = __builtin_bit_cast(v4h, v2u{sw, 0u});
       }
-      if constexpr (PARTIALS) {
+    }
+  };
+  auto fma8 = [](v16f& a, const v16f& p, const v16f& sp, int half) {
+#pragma unroll
+    for (int e = 8 * half; e < 8 * half + 8; ++e) a[e] = __builtin_fmaf(p[e], sp[e], a[e]);
+  };
+  // stage s is complete in LDS for every wave: own loads drained down to the next stage's,
+  // then a barrier (which also frees stage s - 1's buffer for stage s + 2)
+  //  (a bare s_barrier: __syncthreads() would add a fence that drains every load in flight,
+  //  including the next stage's)
+  auto wait_stage = [&](int s) {
+    if (s + 1 < S)
+      SVDQ_WAIT_VMCNT(kLoads);
+    else
+      SVDQ_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if constexpr (PARTIALS) {
+    for (int s = 0; s < S; ++s) {
+      wait_stage(s);
+      if (s + 2 < S) issue_stage(s + 2);
+      const uint8_t* st = lds + (s % NB) * kStage;
+      const int ng = min(KS, G - s * KS);
+      for (int gg = 0; gg < ng; ++gg) {
+        Frag F;
+        read_frag(st, gg, F);
         const int g = s * KS + gg;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], zero16, 3, 3, 0, 127, 0, 127);
+            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.A[i], F.B[j], zero16, 3, 3, 0, 127, 0, 127);
             const int col = n_tile + wn * 64 + 32 * j + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -193,34 +235,68 @@ void w4a4_gemm_e3m2_kernel(
               if (row < M && col < N) P[((size_t)g * M + row) * N + col] = (int32_t)p[e];  // exact
             }
           }
-      } else {
-        v4h SA[2], SB[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint32_t sx = *reinterpret_cast<const uint16_t*>(st + sa_frag + (gg * RT + i) * 128);
-          const uint32_t sw = *reinterpret_cast<const uint16_t*>(st + sb_frag + (gg * CT + i) * 128);
-          SA[i] = __builtin_bit_cast(v4h, v2u{sx, 0u});
-          SB[i] = __builtin_bit_cast(v4h, v2u{sw, 0u});
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[i], B[j], zero16, 3, 3, 0, 127, 0, 127);
-            const v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[i], SB[j], zero16, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], sp[e], acc[i][j][e]);
-            // keep this tile's dequantization here instead of letting the optimizer sink every
-            // FMA below the last MFMA (which would keep all MFMA results live at once)
-            asm volatile("" : "+v"(acc[i][j]));
-            __builtin_amdgcn_sched_barrier(0);
-          }
       }
     }
-    if (s + 1 < S) store_stage((s + 1) & 1, R);
-    __syncthreads();
+    return;
+  } else {
+    // Software pipeline with a lag of one 32 x 32 tile: the 16 FMAs that dequantize tile t are
+    // issued in two halves behind the two MFMAs of tile t + 1, so the VALU works while the
+    // matrix unit does.  The last tile of a stage, (1, 1), is dequantized at the start of the
+    // next stage, under the LDS reads of that stage's first operands.
+    v16f pp = zero16, spp = zero16;  // partial and scale product of the pending tile (1, 1)
+    for (int s = 0; s < S; ++s) {
+      wait_stage(s);
+      if (s + 2 < S) issue_stage(s + 2);
+      const uint8_t* st = lds + (s % NB) * kStage;
+      const int ng = min(KS, G - s * KS);
+      Frag F[KS];
+      read_frag(st, 0, F[0]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e], acc[1][1][e]);
+      asm volatile("" : "+v"(acc[1][1]));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gg = 0; gg < KS; ++gg) {
+        if (gg >= ng) break;  // uniform
+        const Frag& C = F[gg];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = t >> 1, j = t & 1;
+          const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(C.A[i], C.B[j], zero16, 3, 3, 0, 127, 0, 127);
+          // (also in a last stage without a second group: its LDS holds a valid duplicate)
+          if (t == 0 && gg + 1 < KS) read_frag(st, gg + 1, F[gg + 1]);
+          // the pending tile: (1, 1) of the previous group at t == 0, else tile t - 1
+          const int pi = t == 0 ? 1 : (t - 1) >> 1, pj = t == 0 ? 1 : (t - 1) & 1;
+          const bool have = t > 0 || gg > 0;
+          if (have) fma8(acc[pi][pj], pp, spp, 0);
+          const v16f sn = __builtin_amdgcn_mfma_f32_32x32x8f16(C.SA[i], C.SB[j], zero16, 0, 0, 0);
+          if (have) {
+            fma8(acc[pi][pj], pp, spp, 1);
+            asm volatile("" : "+v"(acc[pi][pj]));
+          }
+          pp = pn;
+          spp = sn;
+          // issue order: MFMA (partial of tile t), 8 VALU (first half of the pending tile),
+          // MFMA (scale product of tile t), 8 VALU -- the pending tile's registers stay
+          // distinct from tile t's, and each MFMA runs under the FMAs behind it
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (t == 0 && gg + 1 < KS)  // the next group's operand reads go under this MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e], acc[1][1][e]);
+    // the scale-product MFMA returned 2 s_x s_w: halve (exact)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] *= 0.5f;
   }
-  if constexpr (PARTIALS) return;
 
   // ---- epilogue: low-rank up-projection, bias, store.  The addresses are loop-invariant;
   //      computed before the K loop they would stay live across it, so they go through an
@@ -278,11 +354,17 @@ static hipError_t launch_e3m2_ntr(int ntr, dim3 grid, hipStream_t stream, const 
                                   int32_t* P) {
   switch (ntr) {
 #define SVDQ_E3M2_CASE(n)                                                                      \
-  case n:                                                                                      \
+  case n: {                                                                                    \
+    /* the three resident stages need more than the default 64 KB of dynamic LDS */            \
+    const hipError_t e = hipFuncSetAttribute(                                                  \
+        reinterpret_cast<const void*>(w4a4_gemm_e3m2_kernel<OUT_FP32, PARTIALS, n>),            \
+        hipFuncAttributeMaxDynamicSharedMemorySize, f6::kLds);                                 \
+    if (e != hipSuccess) return e;                                                             \
     hipLaunchKernelGGL((w4a4_gemm_e3m2_kernel<OUT_FP32, PARTIALS, n>), grid, dim3(f6::THREADS), \
                        f6::kLds, stream, xq, x_scales, T, wq, w_scales, L2, bias, M, N, K, Y,   \
                        P);                                                                     \
-    break;
+    break;                                                                                     \
+  }
     SVDQ_E3M2_CASE(0)
     SVDQ_E3M2_CASE(1)
     SVDQ_E3M2_CASE(2)

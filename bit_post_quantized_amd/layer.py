@@ -29,15 +29,16 @@ class PackedWeights:
     inv_lambda: torch.Tensor  # fp32 [K]
     L1t: torch.Tensor         # bf16 [r, K]  (the [K, r] factor stored K-contiguous)
     L2t: torch.Tensor         # bf16 [N, r]  (the [r, N] factor stored r-contiguous)
-    wq: torch.Tensor          # uint8 [N, K/2] (nibbles) or [N, 3K/4] (BF6 codes)
+    wq: torch.Tensor          # uint8 [N, K/2] (nibbles) or the tiled BF6 container of N rows
     w_scales: torch.Tensor    # fp16 [K/64, N]
     bias: Optional[torch.Tensor] = None  # bf16 [N]
     e3m2: bool = False        # container of wq (and of the activation codes in forward)
+    R32: Optional[torch.Tensor] = None  # fp32 [K, N] residual, kept only on request
 
 
 def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
                     bias: Optional[torch.Tensor] = None, device="cuda",
-                    e3m2: bool = False) -> PackedWeights:
+                    e3m2: bool = False, keep_residual: bool = False) -> PackedWeights:
     """W bf16 [K, N] (Y = X W), X_calib bf16 [M, K] calibration activations."""
     K, N = W.shape
     Wd = W.detach().to("cpu", torch.float64)
@@ -62,7 +63,7 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
     R32 = R.to(torch.float32).to(device).contiguous()
     w_scales = torch.empty(K // 64, N, dtype=torch.float16, device=device)
     if e3m2:
-        wq = torch.empty(N, K // 4 * 3, dtype=torch.uint8, device=device)
+        wq = torch.empty(binding.svdq_e3m2_bytes(N, K), dtype=torch.uint8, device=device)
         binding.svdq_pack_weights_e3m2(R32, wq, w_scales)
     else:
         wq = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
@@ -71,7 +72,8 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
         K=K, N=N, rank=rank, inv_lambda=inv32.to(device),
         L1t=L1b.t().contiguous().to(device), L2t=L2b.t().contiguous().to(device),
         wq=wq, w_scales=w_scales,
-        bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2)
+        bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2,
+        R32=R32 if keep_residual else None)
 
 
 @dataclass
@@ -83,7 +85,8 @@ class ActBuffers:
 
 def alloc_act(M: int, K: int, rank: int, device="cuda", e3m2: bool = False) -> ActBuffers:
     return ActBuffers(
-        xq=torch.empty(M, K // 4 * 3 if e3m2 else K // 2, dtype=torch.uint8, device=device),
+        xq=(torch.empty(binding.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device=device) if e3m2
+            else torch.empty(M, K // 2, dtype=torch.uint8, device=device)),
         x_scales=torch.empty(K // 64, M, dtype=torch.float16, device=device),
         T=torch.empty(M, rank, dtype=torch.float32, device=device) if rank > 0 else None)
 

@@ -118,24 +118,29 @@ int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K
                        void* stream);
 
 /*
- * BF6 (E3M2) container.  The *_e3m2 entry points compute exactly the same codes, scales, T and
- * Y as the entry points above; only the byte layout of the codes differs.  Each code is stored
- * as its 6-bit BF6 pattern (OCP Microscaling format E3M2: sign bit 5, exponent bits 4..2 with
- * bias 3, mantissa bits 1..0; every integer in [-8, 8] is exact), and a row of K codes is one
- * little-endian bit stream of 3K/4 bytes in which code k occupies bits 6k .. 6k+5, so 64-group
- * g is the 48-byte record at byte 48 g.  The FP6 matrix units of gfx950 read this container
- * directly (FLUX4 3.2: a small float format on the matrix units avoids the 4-bit unpack),
- * which is why the GEMM that consumes it is the fast path.
+ * BF6 (E3M2) tiled container.  The *_e3m2 entry points compute exactly the same codes, scales,
+ * T and Y as the entry points above; only the container of the codes differs.  Each code is
+ * stored as its 6-bit BF6 pattern (OCP Microscaling format E3M2: sign bit 5, exponent bits 4..2
+ * with bias 3, mantissa bits 1..0; every integer in [-8, 8] is exact).  A [R, K] code matrix
+ * (R = M for activations, N for weights) is stored as ceil(R / 32) row blocks; block b holds,
+ * for each 64-group g in order, 64 slots of 24 bytes; slot s carries the 32 codes of row
+ * 32 b + (s mod 32) at k = 64 g + 32 (s div 32) + i, i = 0..31, as one little-endian 192-bit
+ * stream (code i at bits 6i .. 6i+5).  Rows past R hold zero codes (the quantize/pack calls
+ * write them).  The slot order is the lane order of the gfx950 32 x 32 x 64 FP6 matrix
+ * operand, so the GEMM copies whole blocks (FLUX4 3.2: a small float format on the matrix
+ * units avoids the 4-bit unpack).  Size: svdq_e3m2_bytes(R, K) bytes, 16-byte aligned.
  *
- * svdq_pack_weights_e3m2 — svdq_pack_weights with
- *   wq6       uint8 [N, 3K/4]                                              16B
- * svdq_quantize_act_e3m2 — svdq_quantize_act with
- *   xq6       uint8 [M, 3K/4]                                              16B
+ * svdq_e3m2_bytes — ceil(rows / 32) * (K / 64) * 1536 (0 for rows <= 0 or K not a positive
+ *   multiple of 64).
+ * svdq_pack_weights_e3m2 — svdq_pack_weights writing wq6 (container of N rows) instead of wq.
+ * svdq_quantize_act_e3m2 — svdq_quantize_act writing xq6 (container of M rows) instead of xq.
  * svdq_w4a4_gemm_e3m2 — svdq_w4a4_gemm reading xq6 / wq6 (same Y up to fp32 summation order).
  * svdq_w4a4_partials_e3m2 — test entry: the exact group partials of the same device inner loop
  *   as svdq_w4a4_gemm_e3m2, P int32 [G, M, N].
- * Arguments, shapes, alignment and error behaviour are those of the matching entry point above.
+ * Arguments, shapes, alignment and error behaviour are otherwise those of the matching entry
+ * point above.
  */
+size_t svdq_e3m2_bytes(int rows, int K);
 int svdq_pack_weights_e3m2(const float* R, int K, int N, uint8_t* wq6, uint16_t* w_scales,
                            void* stream);
 int svdq_quantize_act_e3m2(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,

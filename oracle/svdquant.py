@@ -196,6 +196,39 @@ def unpack_e3m2(packed: np.ndarray, K: int) -> np.ndarray:
     return v.astype(np.int8)
 
 
+E3M2_BLOCK_ROWS = 32       # rows per block of the tiled container
+E3M2_SLOT_CODES = 32       # codes per slot (24 bytes)
+
+
+def pack_e3m2_tiled(codes: np.ndarray) -> np.ndarray:
+    """[R, K] int codes -> the tiled BF6 container, uint8 [ceil(R/32), K/64, 64, 24].
+
+    Block b, group g, slot s holds the 32 codes of row 32 b + (s mod 32) at
+    k = 64 g + 32 (s div 32) + i, i = 0..31, as the little-endian 6-bit stream of
+    ``pack_e3m2`` (24 bytes).  Rows past R are zero codes.  (The order of slots within a block
+    is the lane order of the 32 x 32 x 64 FP6 matrix-multiply operand.)
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    R, K = c.shape
+    nb = -(-R // E3M2_BLOCK_ROWS)
+    pad = np.zeros((nb * E3M2_BLOCK_ROWS, K), dtype=np.int64)
+    pad[:R] = c
+    G = K // GROUP
+    # [block, row-in-block, group, half, 32 codes] -> [block, group, half, row-in-block, 32]
+    v = pad.reshape(nb, E3M2_BLOCK_ROWS, G, 2, E3M2_SLOT_CODES).transpose(0, 2, 3, 1, 4)
+    slots = pack_e3m2(v.reshape(-1, E3M2_SLOT_CODES))          # [n_slots, 24]
+    return slots.reshape(nb, G, 2 * E3M2_BLOCK_ROWS, 24)
+
+
+def unpack_e3m2_tiled(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Inverse of ``pack_e3m2_tiled``: the container (any shape of the same bytes) -> [R, K]."""
+    G = K // GROUP
+    nb = -(-R // E3M2_BLOCK_ROWS)
+    b = np.asarray(buf, dtype=np.uint8).reshape(nb * G * 2 * E3M2_BLOCK_ROWS, 24)
+    v = unpack_e3m2(b, E3M2_SLOT_CODES).reshape(nb, G, 2, E3M2_BLOCK_ROWS, E3M2_SLOT_CODES)
+    return v.transpose(0, 3, 1, 2, 4).reshape(nb * E3M2_BLOCK_ROWS, K)[:R]
+
+
 # --------------------------------------------------------------------------- activations
 def smooth_activations(X_bits, inv_lam32: np.ndarray) -> np.ndarray:
     """X^ = fl32(fl32(X) * inv_lam): the smoothing divide as one fp32 multiply by the stored

@@ -26,7 +26,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,6 +80,12 @@ def test_gemm_validation(lib):
     p = lib.svdq_w4a4_partials
     assert p(FAKE, FAKE, 8, 8, 96, FAKE, None) == binding.SVDQ_ESHAPE
     assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
+
+
+def test_e3m2_container_size(lib):
+    assert lib.svdq_e3m2_bytes(4608, 3072) == 144 * 48 * 1536
+    assert lib.svdq_e3m2_bytes(33, 128) == 2 * 2 * 1536
+    assert lib.svdq_e3m2_bytes(0, 128) == 0 and lib.svdq_e3m2_bytes(8, 100) == 0
 
 
 def test_e3m2_entry_points_validate_like_their_nibble_twins(lib):

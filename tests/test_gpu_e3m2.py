@@ -1,8 +1,8 @@
 """GPU parity of the BF6 (E3M2) container path against the CPU oracle, through the C ABI.
 
-The *_e3m2 entry points carry the same INT4 codes as the nibble path in 6-bit BF6 patterns.
-Bar: the packed bytes equal the oracle's codes packed by the oracle's own E3M2 encoder
-(bit-exact), scales bit-exact, the exact group partials bit-exact, T and Y within the
+The *_e3m2 entry points carry the same INT4 codes as the nibble path in 6-bit BF6 patterns,
+in the tiled container.  Bar: the container bytes equal the oracle's codes packed by the
+oracle's own tiled E3M2 packer (bit-exact), scales bit-exact, the exact group partials bit-exact, T and Y within the
 normwise max-abs-rel 1e-2; and the two GEMM routes agree with each other up to fp32
 summation order.
 """
@@ -34,14 +34,15 @@ def _expected(name):
     """The oracle's codes of the case in the E3M2 container (weights, activations)."""
     case = _case(name)
     ref = oracle_act(case)
-    return osq.pack_e3m2(case[2]["codes"]), osq.pack_e3m2(ref["codes"])
+    return (osq.pack_e3m2_tiled(case[2]["codes"]).reshape(-1),
+            osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
 
 
 def _gpu_pack6(case):
     d, pw, packed, r = case
     K, N = pw["R32"].shape
     w = device_weights(case)
-    wq6 = torch.empty(N, K // 4 * 3, dtype=torch.uint8, device="cuda")
+    wq6 = torch.empty(B.svdq_e3m2_bytes(N, K), dtype=torch.uint8, device="cuda")
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
     B.svdq_pack_weights_e3m2(w["R32"], wq6, ws)
     return wq6, ws
@@ -51,7 +52,7 @@ def _gpu_act6(case):
     d, pw, packed, r = case
     M, K = d["X"].shape
     w = device_weights(case)
-    xq6 = torch.empty(M, K // 4 * 3, dtype=torch.uint8, device="cuda")
+    xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
     xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r, dtype=torch.float32, device="cuda") if r else None
     B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), w["inv_lambda"], w["L1t"], r, xq6, xs, T)
@@ -115,13 +116,15 @@ def test_partials_e3m2_bitexact(gpu_lib, name):
     case = _case(name)
     xq6, xs, T = _gpu_act6(case)
     wq6, ws = _gpu_pack6(case)
-    M, N = xq6.shape[0], wq6.shape[0]
-    if name in FULL:  # a row/column slice of the full problem (same kernel, same k loop)
+    d, pw = case[0], case[1]
+    (M, K), N = d["X"].shape, pw["R32"].shape[1]
+    if name in FULL:  # the leading rows / columns of the full problem (a prefix of each container)
         M, N = 160, 200
-        xq6, wq6 = xq6[:M].contiguous(), wq6[:N].contiguous()
-    G = xq6.shape[1] // 48
+        xq6 = xq6[:B.svdq_e3m2_bytes(M, K)]
+        wq6 = wq6[:B.svdq_e3m2_bytes(N, K)]
+    G = K // 64
     P = torch.empty(G, M, N, dtype=torch.int32, device="cuda")
-    B.svdq_w4a4_partials_e3m2(xq6, wq6, P)
+    B.svdq_w4a4_partials_e3m2(xq6, wq6, M, N, K, P)
     torch.cuda.synchronize()
     ref = oracle_act(case)
     np.testing.assert_array_equal(P.cpu().numpy(), osq.int_partials(ref["codes"][:M], case[2]["codes"][:N]))
@@ -148,8 +151,8 @@ def test_e3m2_and_nibble_routes_agree(gpu_lib):
     B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2t"], w["bias"], r, Y4)
     B.svdq_w4a4_gemm_e3m2(xq6, xs6, T6, wq6, ws6, w["L2t"], w["bias"], r, Y6)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(osq.unpack_e3m2(xq6.cpu().numpy(), K), osq.unpack_nibbles(xq.cpu().numpy()))
-    np.testing.assert_array_equal(osq.unpack_e3m2(wq6.cpu().numpy(), K), osq.unpack_nibbles(wq.cpu().numpy()))
+    np.testing.assert_array_equal(osq.unpack_e3m2_tiled(xq6.cpu().numpy(), M, K), osq.unpack_nibbles(xq.cpu().numpy()))
+    np.testing.assert_array_equal(osq.unpack_e3m2_tiled(wq6.cpu().numpy(), N, K), osq.unpack_nibbles(wq.cpu().numpy()))
     assert torch.equal(xs, xs6) and torch.equal(ws, ws6) and torch.equal(T, T6)
     assert max_abs_rel(Y6.cpu().numpy().astype(np.float64), Y4.cpu().numpy().astype(np.float64)) <= 1e-5
 
@@ -166,10 +169,10 @@ def test_e3m2_rank0_unit_scales_reduce_to_exact_integer_gemm(gpu_lib):
     X, Wt = ints(M), ints(N)
     exact = X @ Wt.T
     inv = torch.ones(K, dtype=torch.float32, device="cuda")
-    xq6 = torch.empty(M, K // 4 * 3, dtype=torch.uint8, device="cuda")
+    xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
     xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act_e3m2(dev_bf16(bf16_to_bits(X)), inv, None, 0, xq6, xs, None)
-    wq6 = torch.empty(N, K // 4 * 3, dtype=torch.uint8, device="cuda")
+    wq6 = torch.empty(B.svdq_e3m2_bytes(N, K), dtype=torch.uint8, device="cuda")
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
     B.svdq_pack_weights_e3m2(dev(np.ascontiguousarray(Wt.T).astype(np.float32)), wq6, ws)
     Y32 = torch.empty(M, N, dtype=torch.float32, device="cuda")
@@ -196,14 +199,14 @@ def test_e3m2_clamped_codes_of_subnormal_scales(gpu_lib):
     inv = np.ones(K, np.float32)
     ref = osq.quantize_act(bits, inv, None)
     assert (ref["codes"] == -8).sum() >= M * K // 64 and float(ref["s_x"].max()) == 2.0 ** -24
-    xq6 = torch.empty(M, K // 4 * 3, dtype=torch.uint8, device="cuda")
+    xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
     xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act_e3m2(dev_bf16(bits), dev(inv), None, 0, xq6, xs, None)
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
     xs4 = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act(dev_bf16(bits), dev(inv), None, 0, xq, xs4, None)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(xq6.cpu().numpy(), osq.pack_e3m2(ref["codes"]))
+    np.testing.assert_array_equal(xq6.cpu().numpy(), osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
     np.testing.assert_array_equal(xq.cpu().numpy(), ref["xq"])
 
 
@@ -214,26 +217,27 @@ def test_e3m2_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     pw = osq.prepare_weights(d["X"], d["W"], 0.5, r)
     packed = osq.pack_weights(pw["R32"])
     ref = osq.quantize_act(d["X"], pw["inv_lambda"], pw["L1b"])
-    G, KB = K // 64, K // 4 * 3
+    G = K // 64
+    BW, BX = B.svdq_e3m2_bytes(N, K), B.svdq_e3m2_bytes(M, K)
     GUARD = 0x5A
-    wq6 = torch.full((N + 1, KB), GUARD, dtype=torch.uint8, device="cuda")
+    wq6 = torch.full((BW + 64,), GUARD, dtype=torch.uint8, device="cuda")
     ws = torch.zeros(G * N + 8, dtype=torch.float16, device="cuda")
-    B.svdq_pack_weights_e3m2(dev(pw["R32"]), wq6[:N], ws[:G * N].view(G, N))
-    xq6 = torch.full((M + 1, KB), GUARD, dtype=torch.uint8, device="cuda")
+    B.svdq_pack_weights_e3m2(dev(pw["R32"]), wq6[:BW], ws[:G * N].view(G, N))
+    xq6 = torch.full((BX + 64,), GUARD, dtype=torch.uint8, device="cuda")
     xs = torch.full((G * M + 8,), -3.0, dtype=torch.float16, device="cuda")
     T = torch.full((M + 1, max(r, 1)), -7.0, dtype=torch.float32, device="cuda")
     L1t = dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None
     L2t = dev_bf16(bf16_to_bits(pw["L2b"].T)) if r else None
     Tv = T[:M] if r else None
-    B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq6[:M],
+    B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq6[:BX],
                              xs[:G * M].view(G, M), Tv)
     Y = torch.full((M + 1, N), 3.0, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6[:M], xs[:G * M].view(G, M), Tv, wq6[:N], ws[:G * N].view(G, N),
+    B.svdq_w4a4_gemm_e3m2(xq6[:BX], xs[:G * M].view(G, M), Tv, wq6[:BW], ws[:G * N].view(G, N),
                           L2t, dev_bf16(d["bias"]), r, Y[:M])
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(wq6[:N].cpu().numpy(), osq.pack_e3m2(packed["codes"]))
-    np.testing.assert_array_equal(xq6[:M].cpu().numpy(), osq.pack_e3m2(ref["codes"]))
-    assert (wq6[N].cpu() == GUARD).all() and (xq6[M].cpu() == GUARD).all()
+    np.testing.assert_array_equal(wq6[:BW].cpu().numpy(), osq.pack_e3m2_tiled(packed["codes"]).reshape(-1))
+    np.testing.assert_array_equal(xq6[:BX].cpu().numpy(), osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
+    assert (wq6[BW:].cpu() == GUARD).all() and (xq6[BX:].cpu() == GUARD).all()
     assert (xs[G * M:].cpu() == -3.0).all() and (ws[G * N:].cpu() == 0).all()
     assert (Y[M].cpu().float() == 3.0).all()
     if r:

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from oracle.svdquant import (QMAX, QMIN, e3m2_encode_codes, e3m2_value, pack_e3m2,
-                             quantize_groups, unpack_e3m2)
+                             pack_e3m2_tiled, quantize_groups, unpack_e3m2, unpack_e3m2_tiled)
 
 
 def test_published_limits_of_the_format():
@@ -76,3 +76,37 @@ def test_quantizer_output_fits_the_container():
     v = rng.standard_normal((50, 64)).astype(np.float32) * rng.uniform(1e-3, 1e3, (50, 1)).astype(np.float32)
     q, _ = quantize_groups(v)
     assert np.array_equal(unpack_e3m2(pack_e3m2(q.astype(np.int64)), 64), q)
+
+
+def test_tiled_container_slot_placement_by_hand():
+    # R = 33 rows (two blocks), K = 128 (two groups).  Row 32 is row 0 of block 1; its codes
+    # k = 64..95 (group 1, first half) sit in block 1, group 1, slot 0; k = 96..127 in slot 32.
+    R, K = 33, 128
+    codes = np.zeros((R, K), np.int64)
+    codes[32, 64] = 1        # -> block 1, group 1, slot 0, code 0
+    codes[32, 127] = -8      # -> block 1, group 1, slot 32, code 31
+    codes[5, 40] = 3         # -> block 0, group 0, slot 37 (row 5, second half), code 8
+    t = pack_e3m2_tiled(codes)
+    assert t.shape == (2, 2, 64, 24)
+    assert t[1, 1, 0, 0] == 0x0C and not t[1, 1, 0, 1:].any()
+    # code 31 occupies stream bits 186..191 = the top 6 bits of byte 23
+    assert t[1, 1, 32, 23] == (0x38 << 2) & 0xFF and not t[1, 1, 32, :23].any()
+    # code 8 occupies bits 48..53 = the low 6 bits of byte 6
+    assert t[0, 0, 37, 6] == 0x12
+    assert int(np.count_nonzero(t)) == 3
+    assert not t[1, :, 1:32].any() and not t[1, :, 33:].any()   # rows past R are zero
+
+
+def test_tiled_container_round_trip_and_slot_streams():
+    rng = np.random.default_rng(8)
+    for R, K in [(1, 64), (31, 192), (32, 64), (70, 256)]:
+        codes = rng.integers(-8, 8, size=(R, K))
+        t = pack_e3m2_tiled(codes)
+        assert t.size == -(-R // 32) * (K // 64) * 64 * 24
+        assert np.array_equal(unpack_e3m2_tiled(t, R, K), codes)
+        # every slot is the plain stream of its 32 codes
+        b, g, s = rng.integers(0, t.shape[0]), rng.integers(0, t.shape[1]), rng.integers(0, 64)
+        row = 32 * b + s % 32
+        ks = 64 * g + 32 * (s // 32)
+        want = codes[row, ks:ks + 32] if row < R else np.zeros(32, np.int64)
+        assert np.array_equal(t[b, g, s], pack_e3m2(want[None])[0])
