@@ -155,7 +155,7 @@ int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N
 
 /*
  * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its
- * cross-token min/max reduction: one partial (lo, hi) per channel and 320-token chunk (0 when
+ * cross-token min/max reduction: one partial (lo, hi) per channel and 64-token chunk (0 when
  * tokens == 0).  Its contents need no initialization and carry nothing between calls; calls
  * that share one workspace must not overlap in time (one stream, or one workspace per stream).
  */

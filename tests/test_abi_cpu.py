@@ -110,8 +110,8 @@ def test_e3m2_entry_points_validate_like_their_nibble_twins(lib):
 def test_kv_validation(lib):
     q = lib.kv_int8_quant
     assert lib.kv_int8_workspace_bytes(0, 4096) == 0
-    # lo/hi partials of 32 chunks of 320 tokens
-    assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 32 * 4096 * 4
+    # lo/hi partials of 160 chunks of 64 tokens
+    assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 160 * 4096 * 4
     assert q(FAKE, 16, 12, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
     assert q(FAKE, -1, 16, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
     assert q(FAKE, 16, 16, FAKE, FAKE, FAKE, None, None) == binding.SVDQ_EINVAL

@@ -250,8 +250,8 @@ def _gpu_kv(x_bits):
     return q.cpu().numpy(), s.cpu().numpy(), z.cpu().numpy(), host_u16(out)
 
 
-# (None,)*3 is the full cache [10240, 32, 128]; 12800 tokens is not a multiple of the 320-token
-# range chunk; (1, 2, 8) is a single token of 16 channels
+# (None,)*3 is the full cache [10240, 32, 128]; 1000 and 100 tokens end in a partial 64-token
+# range chunk; 12800 tokens fill 200 chunks; (1, 2, 8) is a single token of 16 channels
 @pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64),
                                    (12800, 32, 128)])
 def test_kv_quant_dequant_bitexact(gpu_lib, shape):
@@ -277,6 +277,39 @@ def test_kv_workspace_needs_no_initialization_and_is_reusable(gpu_lib):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(q.cpu().numpy(), ref["q"])
         np.testing.assert_array_equal(z.cpu().numpy(), ref["zero"])
+
+
+@pytest.mark.parametrize("shape", [(1000, 8, 64), (10240, 32, 128), (5, 1, 64)])
+def test_kv_single_pass_self_contained_path(gpu_lib, shape, monkeypatch):
+    """The single-pass quantizer with its bounded wait forced to time out at once: every block
+    computes its slab's range from x itself.  Same codes as the oracle; (5, 1, 64) has token
+    parts that are empty."""
+    monkeypatch.setenv("SVDQ_KV_SPIN_TICKS", "0")
+    for name, (x, ref) in kv_case(*shape).items():
+        q, s, z, xo = _gpu_kv(x)
+        np.testing.assert_array_equal(q, ref["q"])
+        np.testing.assert_array_equal(z, ref["zero"])
+        np.testing.assert_array_equal(s.view(np.uint32), ref["scale"].view(np.uint32))
+
+
+def test_kv_repeated_calls_share_a_workspace(gpu_lib):
+    """Back-to-back single-pass calls (K, V, K, ...) on one workspace, no synchronization between
+    them: each call's exchange only accepts its own partial ranges."""
+    case = kv_case(1000, 8, 64)
+    ws = torch.full((B.kv_int8_workspace_bytes(1000, 512),), 0xA5, dtype=torch.uint8, device="cuda")
+    outs = []
+    for rep in range(3):
+        for name in ("K", "V"):
+            x, ref = case[name]
+            q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+            s = torch.empty(x.shape[1], dtype=torch.float32, device="cuda")
+            z = torch.empty(x.shape[1], dtype=torch.uint8, device="cuda")
+            B.kv_int8_quant(dev_bf16(x), q, s, z, ws)
+            outs.append((name, q, z))
+    torch.cuda.synchronize()
+    for name, q, z in outs:
+        np.testing.assert_array_equal(q.cpu().numpy(), case[name][1]["q"])
+        np.testing.assert_array_equal(z.cpu().numpy(), case[name][1]["zero"])
 
 
 def test_kv_degenerate_channels(gpu_lib):
