@@ -27,17 +27,19 @@
 
 namespace svdq {
 
-constexpr int kActRows = 16;   // tokens per workgroup
-constexpr int kActBatch = 6;   // groups per wave whose loads are in flight together
+constexpr int kActRows = 16;    // tokens per workgroup
+constexpr int kActBatch = 6;    // groups per wave whose code loads are in flight together
 constexpr int kActMaxWaves = 8;
+constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
-template <int NTR, bool E3M2>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
+template <int NTR, bool E3M2, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
 __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
     uint16_t* __restrict__ x_scales, float* __restrict__ T) {
-  extern __shared__ float red[];  // [nwaves][16][r]
+  extern __shared__ float smem[];  // [K] inv_lambda (when staged), then [nwaves][16][r]
   constexpr int r = 16 * NTR;
+  constexpr int NT = NTR > 0 ? NTR : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -48,35 +50,61 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
   const int row_ld = row < M ? row : M - 1;
   const int G = K / kGroup;
   const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
+  float* lam = smem;
+  float* red = smem + (LAM_LDS ? K : 0);
 
-  v4f acc[NTR > 0 ? NTR : 1];
+  // inv_lambda is shared by every row: one coalesced copy into LDS per workgroup, so the group
+  // loop's only global loads are the activations and L1, and no wait on them also waits for
+  // the code stores (which count in the same counter)
+  if constexpr (LAM_LDS) {
+    for (int i = threadIdx.x; i < K / 4; i += blockDim.x)
+      reinterpret_cast<v4f*>(lam)[i] = reinterpret_cast<const v4f*>(inv_lambda)[i];
+    __syncthreads();
+  }
+
+  v4f acc[NT];
 #pragma unroll
-  for (int t = 0; t < (NTR > 0 ? NTR : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's L1 operands for group g (k = 16 q .. 16 q + 15 of rank rows 16 t + rl)
+  auto load_l1 = [&](int g, v4u (&dst)[NT][2]) {
+    if constexpr (NTR > 0) {
+#pragma unroll
+      for (int t = 0; t < NTR; ++t) {
+        const v4u* bp = reinterpret_cast<const v4u*>(L1 + (size_t)(16 * t + rl) * K + (size_t)g * kGroup + 16 * q);
+        dst[t][0] = bp[0];
+        dst[t][1] = bp[1];
+      }
+    }
+  };
 
   for (int j0 = wave; j0 < G; j0 += kActBatch * nwaves) {
+    // every load of the batch is issued before any of it is used (group index clamped; a
+    // clamped duplicate is computed but neither stored nor accumulated)
     v4u raw[kActBatch][2];
 #pragma unroll
-    for (int b = 0; b < kActBatch; ++b) {  // unconditional loads (group index clamped)
+    for (int b = 0; b < kActBatch; ++b) {
       const int g = min(j0 + b * nwaves, G - 1);
       const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
       raw[b][0] = p[0];
       raw[b][1] = p[1];
     }
+    v4u bfr[2][NT][2];  // L1 operands, one group ahead
+    load_l1(min(j0, G - 1), bfr[0]);
 #pragma unroll
     for (int b = 0; b < kActBatch; ++b) {
-      const int g = j0 + b * nwaves;
-      if (g >= G) break;  // uniform over the wave
+      const int g_raw = j0 + b * nwaves;
+      const bool gv = g_raw < G;  // uniform over the workgroup
+      const int g = gv ? g_raw : G - 1;
+      if (b + 1 < kActBatch) load_l1(min(j0 + (b + 1) * nwaves, G - 1), bfr[(b + 1) & 1]);
       const int k0 = g * kGroup + 16 * q;
-      const v4f* lp = reinterpret_cast<const v4f*>(inv_lambda + k0);
-      const v4f l0 = lp[0], l1 = lp[1], l2 = lp[2], l3 = lp[3];
-      v4u bfr[NTR > 0 ? NTR : 1][2];
-      if constexpr (NTR > 0) {
-#pragma unroll
-        for (int t = 0; t < NTR; ++t) {
-          const v4u* bp = reinterpret_cast<const v4u*>(L1 + (size_t)(16 * t + rl) * K + k0);
-          bfr[t][0] = bp[0];
-          bfr[t][1] = bp[1];
-        }
+      v4f l0, l1, l2, l3;
+      if constexpr (LAM_LDS) {
+        const v4f* lp = reinterpret_cast<const v4f*>(lam + k0);
+        l0 = lp[0]; l1 = lp[1]; l2 = lp[2]; l3 = lp[3];
+      } else {
+        const v4f* lp = reinterpret_cast<const v4f*>(inv_lambda + k0);
+        l0 = lp[0]; l1 = lp[1]; l2 = lp[2]; l3 = lp[3];
       }
       float xh[16];
       {
@@ -117,23 +145,26 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
         const float v = __builtin_amdgcn_fmed3f(rne_quotient(xh[i], s1, rcp), -8.0f, 7.0f);
         c[i] = (zero || !live) ? 0.0f : v + 0.0f;  // + 0 turns a -0 code into +0
       }
-      if constexpr (E3M2) {  // rows up to the block boundary (padding rows get zero codes)
-        uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
-        *reinterpret_cast<v3u*>(dst) = pack16_e3m2(c);
-      }
-      if (live) {
-        if constexpr (!E3M2)
-          *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
-        if (q == 0) x_scales[(size_t)g * M + row] = sb;
+      if (gv) {
+        if constexpr (E3M2) {  // rows up to the block boundary (padding rows get zero codes)
+          uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
+          *reinterpret_cast<v3u*>(dst) = pack16_e3m2(c);
+        }
+        if (live) {
+          if constexpr (!E3M2)
+            *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
+          if (q == 0) x_scales[(size_t)g * M + row] = sb;
+        }
       }
 
-      // ---- low-rank down-projection on bf16 MFMA
+      // ---- low-rank down-projection on bf16 MFMA (a clamped duplicate group adds zero)
       if constexpr (NTR > 0) {
-        const v8bf a0 = to_bf16x8(xh), a1 = to_bf16x8(xh + 8);
+        v8bf a0 = to_bf16x8(xh), a1 = to_bf16x8(xh + 8);
+        if (!gv) a0 = a1 = v8bf{};
 #pragma unroll
         for (int t = 0; t < NTR; ++t) {
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, bfr[t][0]), acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, bfr[t][1]), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, bfr[b & 1][t][0]), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, bfr[b & 1][t][1]), acc[t], 0, 0, 0);
         }
       }
     }
@@ -156,22 +187,25 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
   }
 }
 
-template <bool E3M2>
+template <bool E3M2, bool LAM_LDS>
 static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                              int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                             hipStream_t stream) {
-  const int G = K / kGroup;
-  const int nwaves = G < kActMaxWaves ? G : kActMaxWaves;
-  const size_t lds = (size_t)nwaves * 16 * r * sizeof(float);
+                             int nwaves, size_t lds, hipStream_t stream) {
   // the tiled BF6 container is written up to the next multiple of 32 rows
   const int rows = E3M2 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
   const dim3 grid((rows + kActRows - 1) / kActRows), block(64 * nwaves);
   switch (r / 16) {
 #define SVDQ_ACT_CASE(n)                                                                   \
-  case n:                                                                                  \
-    hipLaunchKernelGGL((quantize_act_kernel<n, E3M2>), grid, block, lds, stream, X,         \
+  case n: {                                                                                \
+    const void* fn = reinterpret_cast<const void*>(quantize_act_kernel<n, E3M2, LAM_LDS>);  \
+    if (lds > 64 * 1024) {                                                                 \
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e != hipSuccess) return e;                                                       \
+    }                                                                                      \
+    hipLaunchKernelGGL((quantize_act_kernel<n, E3M2, LAM_LDS>), grid, block, lds, stream, X, \
                        inv_lambda, L1, M, K, xq, x_scales, T);                             \
-    break;
+    break;                                                                                 \
+  }
     SVDQ_ACT_CASE(0)
     SVDQ_ACT_CASE(1)
     SVDQ_ACT_CASE(2)
@@ -188,11 +222,24 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
   return hipGetLastError();
 }
 
+template <bool E3M2>
+static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
+                                   int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
+                                   hipStream_t stream) {
+  const int G = K / kGroup;
+  const int nwaves = G < kActMaxWaves ? G : kActMaxWaves;
+  const size_t red = (size_t)nwaves * 16 * r * sizeof(float);
+  const size_t lam = (size_t)K * sizeof(float);
+  if (lam + red <= kActLdsLambda)
+    return launch_act<E3M2, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red, stream);
+  return launch_act<E3M2, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, stream);
+}
+
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                                int e3m2, hipStream_t stream) {
-  return e3m2 ? launch_act<true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream)
-              : launch_act<false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
+  return e3m2 ? launch_act_route<true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream)
+              : launch_act_route<false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
 }
 
 }  // namespace svdq

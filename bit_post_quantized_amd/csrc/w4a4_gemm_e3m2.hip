@@ -23,9 +23,9 @@
 //    are issued while stage s is computed.  The tiled container's blocks are copied as they
 //    are, so an MFMA operand is three ds_read_b64 per lane from its 24-byte slot.
 //  * Scale products.  s_x[m] * s_w[n] for a 32 x 32 tile is an outer product that
-//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) from fp16 pairs
-//    read straight from LDS (see the operand note in the kernel); the factor 2 it carries is
-//    removed once at the end.  The dequantization is one FMA per output and group.
+//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) from one fp16 per
+//    lane read straight from LDS, with every k-slot but one zero (see the operand note in the
+//    kernel).  The dequantization is one FMA per output and group.
 //  * Epilogue.  bf16(T) [32 x 16] and L2 [16 x 32] fragments go through
 //    v_mfma_f32_32x32x16_bf16 with the fp32 accumulator as C, then the bias is added and the
 //    tile is rounded to bf16 (or kept fp32) and stored.
@@ -152,13 +152,13 @@ void w4a4_gemm_e3m2_kernel(
     b_base[i] = kScA + kScB + kOpA + ((2 * wn + i) * KS) * kFrag + lane * 24;
     asm volatile("" : "+v"(a_base[i]), "+v"(b_base[i]));
   }
-  // scale-product operands (v_mfma_f32_32x32x8_f16, fp16 pairs): A gets the dwords of rows
-  // r and r + 1 -- (s_x[r], 0, s_x[r+1], 0) -- and B gets (s_w[n], 0, 0, 0) from its dword and
-  // a zero, so the product of k-slot pairs is s_x[r] s_w[n] + s_x[r+1] * 0; both lane
-  // halves hold the same values, so the MFMA returns exactly 2 s_x s_w.  (Row r + 1 of the
-  // last s_x entry is the first s_w entry: a finite fp16 value times zero.)
+  // scale-product operands (v_mfma_f32_32x32x8_f16): lane l supplies k-slots 4 (l / 32) .. +3
+  // of row (column) l % 32.  A is (s_x[row], 0, 0, 0) -- the zero-extended dword of s_x and a
+  // zero dword -- and B is (s_w[col], 0, 0, 0), both in lanes 0..31 only (zeros in lanes
+  // 32..63), so only k-slot 0 contributes and the MFMA returns s_x[row] * s_w[col] exactly.
   const int sa_off = (32 * 2 * wm + (lane & 31)) * 4;            // + (gg * TM + 32 i) * 4
   const int sb_off = kScA + (32 * 2 * wn + (lane & 31)) * 4;    // + (gg * TN + 32 j) * 4
+  const uint32_t sb_keep = lane < 32 ? 0xFFFFFFFFu : 0u;
 
   v16f acc[2][2];
 #pragma unroll
@@ -188,10 +188,10 @@ void w4a4_gemm_e3m2_kernel(
       F.A[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
       F.B[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, 0, 0};
       if constexpr (!PARTIALS) {
-        const v2u sx = *reinterpret_cast<const v2u*>(st + sa_off + (gg * TM + 32 * i) * 4);
+        const uint32_t sx = *reinterpret_cast<const uint32_t*>(st + sa_off + (gg * TM + 32 * i) * 4);
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + sb_off + (gg * TN + 32 * i) * 4);
-        F.SA[i] = __builtin_bit_cast(v4h, sx);
-        F.SB[i] = __builtin_bit_cast(v4h, v2u{sw, 0u});
+        F.SA[i] = __builtin_bit_cast(v4h, v2u{sx & sb_keep, 0u});
+        F.SB[i] = __builtin_bit_cast(v4h, v2u{sw & sb_keep, 0u});
       }
     }
   };
@@ -291,11 +291,6 @@ void w4a4_gemm_e3m2_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e], acc[1][1][e]);
-    // the scale-product MFMA returned 2 s_x s_w: halve (exact)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] *= 0.5f;
   }
 
   // ---- epilogue: low-rank up-projection, bias, store.  The addresses are loop-invariant;

@@ -71,6 +71,31 @@ def test_quantize_act_bitexact_codes_and_lowrank(gpu_lib, name):
     assert err <= TOL, err
 
 
+def test_quantize_act_long_k_both_containers(gpu_lib):
+    # K = 24576: the smoothing factors no longer fit the activation kernel's LDS budget beside
+    # the rank-32 reduction area, so it reads them from global memory instead.  Both code
+    # containers, codes and scales bit-exact, T within tolerance.
+    case = linear_case(4, 40, 24576, 64)
+    d, pw, packed, r = case
+    M, K = d["X"].shape
+    w = device_weights(case)
+    X = dev_bf16(d["X"])
+    ref = oracle_act(case)
+    xq, xs, T = _gpu_act(case)
+    xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
+    xs6 = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    T6 = torch.empty(M, r, dtype=torch.float32, device="cuda")
+    B.svdq_quantize_act_e3m2(X, w["inv_lambda"], w["L1t"], r, xq6, xs6, T6)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xq.cpu().numpy(), ref["xq"])
+    np.testing.assert_array_equal(xq6.cpu().numpy(), osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
+    want_s = np.ascontiguousarray(ref["s_x"].T).view(np.uint16)
+    np.testing.assert_array_equal(host_u16(xs), want_s)
+    np.testing.assert_array_equal(host_u16(xs6), want_s)
+    assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
+    assert max_abs_rel(T6.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
+
+
 def _rows_for(M, full):
     if not full:
         return np.arange(M)
