@@ -60,6 +60,11 @@ static_assert(kStage % 16 == 0, "16-byte aligned stages");
 
 #define SVDQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding: vmcnt in bits 3..0
 // and 15..14, expcnt 6..4, lgkmcnt 11..8)
 #define SVDQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -139,6 +144,31 @@ void w4a4_gemm_e3m2_kernel(
     }
   };
 
+  // Load idx (0 .. kLoads - 1) of stage s alone: the main loop spreads a stage's loads over the
+  // tiles of the stage before (one behind each tile's first MFMA) instead of issuing them in
+  // one burst, which would hold the wave at the memory pipeline ahead of its MFMAs.
+  // Order: A0, B0, A1, B1, A2, B2, then the s_x and s_w scales.
+  static_assert(kLoadsA == kLoadsB && 2 * kLoadsA + 2 <= KS * 4, "one load per tile");
+  auto issue_load = [&](int s, int idx) {
+    uint8_t* st = lds + (s % NB) * kStage;
+    const int g0 = s * KS;
+    const bool full = g0 + KS <= G;  // every stage but the last one of an odd G
+    if (idx < 2 * kLoadsA) {
+      const int j = idx >> 1;
+      const size_t go = (size_t)(full ? g0 : min(g0 + a_g[j], G - 1) - a_g[j]) * kFrag;
+      if (idx & 1)
+        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
+    } else if constexpr (!PARTIALS) {
+      const int g = full ? g0 : min(g0 + s_gq, G - 1) - s_gq;
+      if (idx == 2 * kLoadsA)
+        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
+    }
+  };
+
   // ---- per-lane read offsets inside a stage.  MFMA operand of 32-row tile i, group gg: lane
   //      l reads its 24-byte slot at +0, +8, +16 (consecutive lanes 24 bytes apart: the 16
   //      lanes of a read phase hit 32 distinct banks).
@@ -156,7 +186,11 @@ void w4a4_gemm_e3m2_kernel(
   // of row (column) l % 32.  A is (s_x[row], 0, 0, 0) -- the zero-extended dword of s_x and a
   // zero dword -- and B is (s_w[col], 0, 0, 0), both in lanes 0..31 only (zeros in lanes
   // 32..63), so only k-slot 0 contributes and the MFMA returns s_x[row] * s_w[col] exactly.
-  const int sa_off = (32 * 2 * wm + (lane & 31)) * 4;            // + (gg * TM + 32 i) * 4
+  // Rows are read pairwise swapped ((l % 32) ^ 1): element e of the scale product then belongs
+  // to element e ^ 1 of the partial, so the dequantization FMA acc[e] += p[e] * s[e ^ 1] reads
+  // its three operands from different VGPR banks (acc, p and s are 16-register tiles whose
+  // element e would otherwise share bank e % 4, which stalls the FMA).
+  const int sa_off = (32 * 2 * wm + ((lane & 31) ^ 1)) * 4;      // + (gg * TM + 32 i) * 4
   const int sb_off = kScA + (32 * 2 * wn + (lane & 31)) * 4;    // + (gg * TN + 32 j) * 4
   const uint32_t sb_keep = lane < 32 ? 0xFFFFFFFFu : 0u;
 
@@ -172,6 +206,33 @@ void w4a4_gemm_e3m2_kernel(
   const int S = (G + KS - 1) / KS;
   issue_stage(0);
   if (S > 1) issue_stage(1);
+
+  // ---- epilogue operands staged in LDS while the last stages run.  From iteration
+  //      max(S - 2, 0) on, buffer S % NB holds no stage any more; T [128 rows x r] fp32,
+  //      L2 [128 cols x r] bf16 and the bias of the tile are copied into it with the same
+  //      direct-to-LDS loads, chunk-column-major (16-byte chunk c of row x at chunk index
+  //      c * 128 + x) so that the epilogue's fragment reads are conflict-free.  (Without a bias
+  //      the bias slot loads the weight scales instead, so every wave issues the same count.)
+  constexpr bool PRE = !PARTIALS && NTR > 0 && NTR * (TM * 16 * 4 + TN * 16 * 2) + TN * 4 <= kStage;
+  constexpr int kPreT = 2 * NTR, kPreL = NTR, kPre = kPreT + kPreL + 1;  // loads per thread
+  constexpr int kPreL2Off = NTR * TM * 16 * 4, kPreBiasOff = kPreL2Off + NTR * TN * 16 * 2;
+  auto issue_prefetch = [&]() {
+    if constexpr (PRE) {
+      uint8_t* pb = lds + (S % NB) * kStage;
+#pragma unroll
+      for (int j = 0; j < kPreT; ++j) {
+        const int p = j * THREADS + tid, c = p / TM, x = p % TM;
+        __builtin_amdgcn_global_load_lds(T + (size_t)min(m_tile + x, M - 1) * r + 4 * c, SVDQ_LDS(pb + j * 4096 + wave * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kPreL; ++j) {
+        const int p = j * THREADS + tid, c = p / TN, x = p % TN;
+        __builtin_amdgcn_global_load_lds(L2 + (size_t)min(n_tile + x, N - 1) * r + 8 * c, SVDQ_LDS(pb + kPreL2Off + j * 4096 + wave * 1024), 16, 0, 0);
+      }
+      const int bc = min(n_tile + (wave & 1) * 64 + lane, N - 1);
+      __builtin_amdgcn_global_load_lds(bias ? bias + bc : w_scales + bc, SVDQ_LDS(pb + kPreBiasOff + (wave & 1) * 256), 2, 0, 0);
+    }
+  };
 
   // one group's MFMA operands, read from LDS
   struct Frag {
@@ -197,7 +258,7 @@ void w4a4_gemm_e3m2_kernel(
   };
   auto fma8 = [](v16f& a, const v16f& p, const v16f& sp, int half) {
 #pragma unroll
-    for (int e = 8 * half; e < 8 * half + 8; ++e) a[e] = __builtin_fmaf(p[e], sp[e], a[e]);
+    for (int e = 8 * half; e < 8 * half + 8; ++e) a[e] = __builtin_fmaf(p[e], sp[e ^ 1], a[e]);
   };
   // stage s is complete in LDS for every wave: own loads drained down to the next stage's,
   // then a barrier (which also frees stage s - 1's buffer for stage s + 2)
@@ -206,6 +267,8 @@ void w4a4_gemm_e3m2_kernel(
   auto wait_stage = [&](int s) {
     if (s + 1 < S)
       SVDQ_WAIT_VMCNT(kLoads);
+    else if (PRE && S >= 2)  // the epilogue's prefetch, issued a stage earlier, may stay in flight
+      SVDQ_WAIT_VMCNT(kPre);
     else
       SVDQ_WAIT_VMCNT(0);
     asm volatile("" ::: "memory");
@@ -244,25 +307,29 @@ void w4a4_gemm_e3m2_kernel(
     // matrix unit does.  The last tile of a stage, (1, 1), is dequantized at the start of the
     // next stage, under the LDS reads of that stage's first operands.
     v16f pp = zero16, spp = zero16;  // partial and scale product of the pending tile (1, 1)
-    for (int s = 0; s < S; ++s) {
+    // one stage; ISSUE: the loads of stage s + 2 are issued one per tile (every stage but the
+    // last two)
+    auto stage = [&](int s, auto issue_tag) {
+      constexpr bool ISSUE = decltype(issue_tag)::value;
       wait_stage(s);
-      if (s + 2 < S) issue_stage(s + 2);
+      if (s == max(S - 2, 0)) issue_prefetch();
       const uint8_t* st = lds + (s % NB) * kStage;
       const int ng = min(KS, G - s * KS);
       Frag F[KS];
       read_frag(st, 0, F[0]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e], acc[1][1][e]);
+      for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e ^ 1], acc[1][1][e]);
       asm volatile("" : "+v"(acc[1][1]));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int gg = 0; gg < KS; ++gg) {
-        if (gg >= ng) break;  // uniform
+        if (gg >= ng) break;  // uniform (only in the last stage, which issues nothing)
         const Frag& C = F[gg];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int i = t >> 1, j = t & 1;
+          const int i = t >> 1, j = t & 1, li = gg * 4 + t;
           const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(C.A[i], C.B[j], zero16, 3, 3, 0, 127, 0, 127);
+          if (ISSUE && li < kLoads) issue_load(s + 2, li);
           // (also in a last stage without a second group: its LDS holds a valid duplicate)
           if (t == 0 && gg + 1 < KS) read_frag(st, gg + 1, F[gg + 1]);
           // the pending tile: (1, 1) of the previous group at t == 0, else tile t - 1
@@ -276,10 +343,11 @@ void w4a4_gemm_e3m2_kernel(
           }
           pp = pn;
           spp = sn;
-          // issue order: MFMA (partial of tile t), 8 VALU (first half of the pending tile),
-          // MFMA (scale product of tile t), 8 VALU -- the pending tile's registers stay
-          // distinct from tile t's, and each MFMA runs under the FMAs behind it
+          // issue order: MFMA (partial of tile t), the stage load, 8 VALU (first half of the
+          // pending tile), MFMA (scale product of tile t), 8 VALU -- the pending tile's
+          // registers stay distinct from tile t's, and each MFMA runs under the work behind it
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ISSUE && li < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           if (t == 0 && gg + 1 < KS)  // the next group's operand reads go under this MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
@@ -288,9 +356,12 @@ void w4a4_gemm_e3m2_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+    };
+    int s = 0;
+    for (; s + 2 < S; ++s) stage(s, BoolTag<true>{});
+    for (; s < S; ++s) stage(s, BoolTag<false>{});
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e], acc[1][1][e]);
+    for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e ^ 1], acc[1][1][e]);
   }
 
   // ---- epilogue: low-rank up-projection, bias, store.  The addresses are loop-invariant;
@@ -299,7 +370,36 @@ void w4a4_gemm_e3m2_kernel(
   int row0 = m_tile + wm * 64, col0 = n_tile + wn * 64, Mo = M, No = N;
   asm volatile("" : "+v"(row0), "+v"(col0), "+s"(Mo), "+s"(No));
   const int l32 = lane & 31, hi = lane >> 5;
-  if constexpr (NTR > 0) {
+  const uint8_t* pb = lds + (S % NB) * kStage;
+  if constexpr (PRE) {  // the staged T, L2 and bias are complete for every wave
+    SVDQ_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  if constexpr (PRE) {
+#pragma unroll
+    for (int kk = 0; kk < r; kk += 16) {
+      const int k8 = kk + 8 * hi;  // this lane's 8 rank indices: T chunks k8 / 4 and + 1
+      v8bf Bt[2], At[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        Bt[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(pb + kPreL2Off + ((k8 / 8) * TN + wn * 64 + 32 * j + l32) * 16));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int x = wm * 64 + 32 * i + l32;
+        const v4f t0 = *reinterpret_cast<const v4f*>(pb + ((k8 / 4) * TM + x) * 16);
+        const v4f t1 = *reinterpret_cast<const v4f*>(pb + ((k8 / 4 + 1) * TM + x) * 16);
+        const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        At[i] = to_bf16x8(tv);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[i], Bt[j], acc[i][j], 0, 0, 0);
+    }
+  } else if constexpr (NTR > 0) {
 #pragma unroll
     for (int kk = 0; kk < r; kk += 16) {
       const int k8 = kk + 8 * hi;  // this lane's 8 rank indices
@@ -324,7 +424,13 @@ void w4a4_gemm_e3m2_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = col0 + 32 * j + l32;
-    const float bj = bias ? bf16_bits_to_float(bias[min(col, No - 1)]) : 0.0f;
+    float bj = 0.0f;
+    if (bias) {
+      if constexpr (PRE)
+        bj = bf16_bits_to_float((uint16_t)*reinterpret_cast<const uint32_t*>(pb + kPreBiasOff + (wn * 64 + 32 * j + l32) * 4));
+      else
+        bj = bf16_bits_to_float(bias[min(col, No - 1)]);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll

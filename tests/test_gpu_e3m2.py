@@ -111,6 +111,24 @@ def test_gemm_e3m2_output_within_tolerance(gpu_lib, name, bias):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("cid", [1, 2])      # rank 16 and rank 32
+@pytest.mark.parametrize("K", [64, 192, 320])  # one, two (ragged) and three (ragged) stages
+def test_gemm_e3m2_short_k(gpu_lib, cid, K):
+    # few K stages: the epilogue operands are staged from the first or a middle iteration
+    case = linear_case(cid, 70, K, 100, True)
+    d, pw, packed, r = case
+    w = device_weights(case)
+    wq6, ws = _gpu_pack6(case)
+    xq6, xs, T = _gpu_act6(case)
+    Y = torch.empty(70, 100, dtype=torch.bfloat16, device="cuda")
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2t"], w["bias"], r, Y)
+    torch.cuda.synchronize()
+    ref = oracle_act(case)
+    Y_ref = osq.linear_output(ref["codes"], ref["s_x"], packed["codes"], packed["s_w"],
+                              ref["T"], pw["L2b"], d["bias"])
+    assert max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref) <= TOL
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_partials_e3m2_bitexact(gpu_lib, name):
     case = _case(name)
