@@ -51,7 +51,31 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=M,
                     help="token rows of the oracle's CPU baseline sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="first copy MB megabytes device to device once (a plain copy of known "
+                         "size, the reference for the HBM byte counters of a profiler run)")
     return ap.parse_args()
+
+
+# HBM traffic of the GEMM kernel per launch, measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, each scaled by what the same counter reads for a plain copy of known size).  The
+# measurement is recorded with the SHA-256 of the kernel source it was taken on; a different
+# source reports no traffic.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "w4a4_gemm_e3m2_ffn_up_4608x3072x12288_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "bit_post_quantized_amd", "csrc", "w4a4_gemm_e3m2.hip")
+
+
+def recorded_traffic():
+    import hashlib
+    try:
+        rec = dict(line.split(":", 1) for line in open(TRAFFIC_RECORD).read().splitlines()
+                   if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256", "").strip() != src:
+        return None
+    return int(rec["traffic_bytes_per_launch"].strip())
 
 
 def algorithmic_bytes():
@@ -139,6 +163,13 @@ def main():
 
     stream = torch.cuda.current_stream()
     names = ["act", "gemm", "kv_quant", "kv_dequant"]
+    if args.copy_probe > 0:
+        n = args.copy_probe * 1024 * 1024 // 4   # fp32 elements: read MB, write MB (a negation)
+        src_b = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_b = torch.empty(n, dtype=torch.float32, device=dev)
+        torch.neg(src_b, out=dst_b)
+        torch.cuda.synchronize()
+        del src_b, dst_b
 
     def step(i, ev=None):
         b = i % ROTATE
@@ -228,7 +259,8 @@ def main():
                    "kv_tokens": KV_T, "kv_heads": KV_H, "kv_dim": KV_D},
         "roofline": {"bound": "mfma", "kernel": "w4a4_gemm_e3m2", "achieved": round(gemm_tops, 2),
                      "peak": FP6_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / FP6_PEAK_TOPS, 4), "traffic": None},
+                     "frac": round(gemm_tops / FP6_PEAK_TOPS, 4), "traffic": recorded_traffic(),
+                     "algorithmic_bytes": ab["gemm"]},
         "cpu_baseline": cpu,
         "pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
         "kv_quant_GBps": round(gbps["kv_quant"], 1),
