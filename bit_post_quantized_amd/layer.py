@@ -13,6 +13,7 @@ the GEMM on the FP6 matrix units (same codes, scales and result; the faster path
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass
 from typing import Optional
 
@@ -34,6 +35,18 @@ class PackedWeights:
     bias: Optional[torch.Tensor] = None  # bf16 [N]
     e3m2: bool = False        # container of wq (and of the activation codes in forward)
     R32: Optional[torch.Tensor] = None  # fp32 [K, N] residual, kept only on request
+    lam: Optional[torch.Tensor] = None  # fp32 [K] smoothing factors (host), for adapters
+
+
+def _bf16_rn(x: torch.Tensor) -> torch.Tensor:
+    """float64 -> bf16 with one round-to-nearest-even: round to odd into fp32 (24 bits keep
+    the two extra bits that make the second rounding exact), then fp32 -> bf16 (RNE)."""
+    x = x.to(torch.float64)
+    t = x.to(torch.float32)
+    over = t.to(torch.float64).abs() > x.abs()
+    t = torch.where(over, torch.nextafter(t, torch.zeros_like(t)), t)  # toward zero
+    inexact = (t.to(torch.float64) != x).to(torch.int32)
+    return (t.view(torch.int32) | inexact).view(torch.float32).to(torch.bfloat16)
 
 
 def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
@@ -53,8 +66,8 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
     W_hat = lam32.to(torch.float64)[:, None] * Wd
     if rank > 0:
         U, S, Vh = torch.linalg.svd(W_hat, full_matrices=False)
-        L1b = (U[:, :rank] * S[:rank]).to(torch.float32).to(torch.bfloat16)
-        L2b = Vh[:rank, :].to(torch.float32).to(torch.bfloat16)
+        L1b = _bf16_rn(U[:, :rank] * S[:rank])
+        L2b = _bf16_rn(Vh[:rank, :])
         R = W_hat - L1b.to(torch.float64) @ L2b.to(torch.float64)
     else:
         L1b = torch.zeros(K, 0, dtype=torch.bfloat16)
@@ -73,7 +86,33 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
         L1t=L1b.t().contiguous().to(device), L2t=L2b.t().contiguous().to(device),
         wq=wq, w_scales=w_scales,
         bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2,
-        R32=R32 if keep_residual else None)
+        R32=R32 if keep_residual else None, lam=lam32)
+
+
+def attach_lora(pw: PackedWeights, A: torch.Tensor, B: torch.Tensor,
+                scale: float = 1.0) -> PackedWeights:
+    """Attach a low-rank adapter W' = W + scale * A B (A [K, r_l], B [r_l, N]) to the 16-bit
+    branch without re-quantizing the 4-bit residual (SVDQ "feature list": LoRA adapters
+    integrate without re-quantization).
+
+    The branch runs on X^ = X diag(lam)^-1, so the adapter joins it as extra rank in the smoothed
+    frame: L1' = [L1 | bf16(lam * A)], L2' = [L2 ; bf16(scale * B)].  The packed codes and
+    scales are shared with ``pw``; the combined rank must stay a multiple of 16, at most 128.
+    """
+    if pw.lam is None:
+        raise ValueError("attach_lora needs the smoothing factors (weights from convert_weights)")
+    K, rl = A.shape
+    if K != pw.K or B.shape != (rl, pw.N):
+        raise ValueError(f"adapter shapes {tuple(A.shape)} x {tuple(B.shape)} do not fit K={pw.K}, N={pw.N}")
+    r2 = pw.rank + rl
+    if r2 % 16 or r2 > 128:
+        raise ValueError(f"combined rank {r2} must be a multiple of 16 and at most 128")
+    dev = pw.L1t.device
+    A_hat = _bf16_rn(pw.lam.to("cpu", torch.float64)[:, None] * A.to("cpu", torch.float64))
+    B_s = _bf16_rn(scale * B.to("cpu", torch.float64))
+    L1t = torch.cat([pw.L1t, A_hat.t().to(dev)], dim=0).contiguous()
+    L2t = torch.cat([pw.L2t, B_s.t().to(dev)], dim=1).contiguous()
+    return dataclasses.replace(pw, rank=r2, L1t=L1t, L2t=L2t)
 
 
 @dataclass

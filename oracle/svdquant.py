@@ -83,6 +83,22 @@ def prepare_weights(X_bits, W_bits, alpha: float, rank: int) -> dict:
     return out
 
 
+def attach_lora(L1b, L2b, lam32, A, B, scale: float = 1.0):
+    """A low-rank adapter joins the 16-bit branch; the 4-bit residual is not re-quantized
+    (SVDQ "feature list": LoRA adapters integrate without re-quantization).
+
+    The adapter changes the layer to W' = W + scale * A B with A [K, r_l], B [r_l, N].  In the
+    smoothed frame W^' = diag(lam) W' = W^ + (diag(lam) A)(scale B), and since the branch runs on
+    X^ = X diag(lam)^-1 it computes X^ (diag(lam) A)(scale B) = scale * X A B.  So the adapter is
+    appended as extra rank: L1' = [L1b | bf16(lam32 * A)], L2' = [L2b ; bf16(scale * B)].
+    Returns (L1', L2') as float64 arrays holding bf16 values.
+    """
+    A_hat = round_bf16(np.asarray(lam32, dtype=np.float64)[:, None] * np.asarray(A, dtype=np.float64))
+    B_s = round_bf16(scale * np.asarray(B, dtype=np.float64))
+    return (np.concatenate([np.asarray(L1b, dtype=np.float64), A_hat], axis=1),
+            np.concatenate([np.asarray(L2b, dtype=np.float64), B_s], axis=0))
+
+
 # --------------------------------------------------------------------------- 4-bit quantizer
 def quantize_groups(V32: np.ndarray):
     """Symmetric INT4 quantization of each length-64 vector along the last axis
