@@ -258,7 +258,7 @@ def main():
                    "M": M, "K": K, "N": N, "rank": RANK, "group": 64,
                    "kv_tokens": KV_T, "kv_heads": KV_H, "kv_dim": KV_D},
         "roofline": {"bound": "mfma", "kernel": "w4a4_gemm_e3m2", "achieved": round(gemm_tops, 2),
-                     "peak": FP6_PEAK_TOPS, "unit": "TOP/s",
+                     "peak": FP6_PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tops / FP6_PEAK_TOPS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes": ab["gemm"]},
         "cpu_baseline": cpu,
