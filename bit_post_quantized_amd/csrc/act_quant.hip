@@ -135,24 +135,29 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
       const uint16_t sb = int4_scale_bits(amax);
       const float s = half_bits_to_float(sb);
-      const bool zero = s == 0.0f;
-      const float s1 = zero ? 1.0f : s;
-      const float rcp = 1.0f / s1;
+      const float s1 = s == 0.0f ? 1.0f : s;  // an all-zero group: every quotient is 0
       const bool live = row < M;
-      float c[16];
+      // padding rows get 1 / s = 0: every quotient is then exactly 0, so no select per code
+      const float rcp = live ? 1.0f / s1 : 0.0f;
+      // code + 8 as bytes: rne of the correctly rounded quotient, + 8, clamp to [0, 15]
+      // (a -0 quotient becomes +8 here, so both zeros give the code 0)
+      uint32_t bq[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = __builtin_amdgcn_fmed3f(rne_quotient(xh[i], s1, rcp), -8.0f, 7.0f);
-        c[i] = (zero || !live) ? 0.0f : v + 0.0f;  // + 0 turns a -0 code into +0
+      for (int d = 0; d < 4; ++d) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[4 * d + i], s1, rcp) + 8.0f, 0.0f, 15.0f);
+        bq[d] = bytes4(v);
       }
       if (gv) {
         if constexpr (E3M2) {  // rows up to the block boundary (padding rows get zero codes)
           uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
-          *reinterpret_cast<v3u*>(dst) = pack16_e3m2(c);
+          *reinterpret_cast<v3u*>(dst) = pack16_bf6_biased(bq);
         }
         if (live) {
           if constexpr (!E3M2)
-            *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{pack8_nibbles(c), pack8_nibbles(c + 8)};
+            *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{nibbles8_biased(bq[0], bq[1]), nibbles8_biased(bq[2], bq[3])};
           if (q == 0) x_scales[(size_t)g * M + row] = sb;
         }
       }

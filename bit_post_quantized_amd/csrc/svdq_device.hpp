@@ -113,6 +113,55 @@ __device__ __forceinline__ v3u pack16_e3m2(const float* c) {
   return v3u{w0, w1, w2};
 }
 
+// ---------------------------------------------------------------- codes as biased bytes
+// The activation pass turns each code c in [-8, 7] into the byte c + 8 (v_cvt_pk_u8_f32 of an
+// exact small integer), then derives either container from four bytes at a time.
+
+// Four fp32 holding integers in [0, 15] -> one dword of bytes, value i in byte i.
+__device__ __forceinline__ uint32_t bytes4(const float* v) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(v[i], i, w);
+  return w;
+}
+
+// Eight biased codes (two dwords of bytes) -> one dword of nibbles, code i in bits 4i .. 4i+3,
+// two's complement: OR each dword with itself shifted by 4 so bytes 0 and 2 hold two codes
+// each, gather those bytes with v_perm_b32, and flip bit 3 of every nibble (c + 8 xor 8 is the
+// 4-bit two's complement of c).
+__device__ __forceinline__ uint32_t nibbles8_biased(uint32_t lo, uint32_t hi) {
+  const uint32_t x = lo | (lo >> 4), y = hi | (hi >> 4);
+  return __builtin_amdgcn_perm(y, x, 0x06040200u) ^ 0x88888888u;
+}
+
+// Four biased codes (bytes c + 8) -> four BF6 (E3M2) patterns, one per byte, by table lookup.
+// v_perm_b32 returns, per selector byte 0..7, that byte of the 8-byte pool {src0, src1} (src1
+// holds bytes 0..3); selector 0x0C gives 0x00 and 0x0D gives 0xFF.  One table holds the
+// patterns of c = -8..-1, one those of c = 0..7 (0x00 0C 10 12 14 15 16 17: 0, 1, 2, 3, 4, 5,
+// 6, 7; the negative ones add the sign bit 0x20, -8 is 0x38), and bit 3 of each byte picks
+// between them through a byte mask made by a third v_perm_b32.
+__device__ __forceinline__ uint32_t bf6_of_biased4(uint32_t b) {
+  const uint32_t sel = b & 0x07070707u;
+  const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, sel);
+  const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, sel);
+  const uint32_t msk = __builtin_amdgcn_perm(0u, 0u, ((b >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  return (pos & msk) | (neg & ~msk);
+}
+
+// Four 6-bit patterns in bytes -> one 24-bit run, pattern i at bits 6i.
+__device__ __forceinline__ uint32_t pack4_bf6(uint32_t p) {
+  const uint32_t t = (p & 0x003F003Fu) | ((p >> 2) & 0x0FC00FC0u);  // p0 | p1<<6 | p2<<16 | p3<<22
+  return (t & 0xFFFu) | ((t >> 4) & 0xFFF000u);
+}
+
+// Sixteen biased codes (four dwords of bytes) -> three dwords of the BF6 stream (code i at bits
+// 6i .. 6i+5), the same stream pack16_e3m2 writes.
+__device__ __forceinline__ v3u pack16_bf6_biased(const uint32_t* b) {
+  const uint32_t c0 = pack4_bf6(bf6_of_biased4(b[0])), c1 = pack4_bf6(bf6_of_biased4(b[1]));
+  const uint32_t c2 = pack4_bf6(bf6_of_biased4(b[2])), c3 = pack4_bf6(bf6_of_biased4(b[3]));
+  return v3u{c0 | (c1 << 24), (c1 >> 8) | (c2 << 16), (c2 >> 16) | (c3 << 8)};
+}
+
 // Eight fp32 -> eight bf16 (round to nearest even, v_cvt_pk_bf16_f32) as an MFMA operand.
 __device__ __forceinline__ v8bf to_bf16x8(const float* x) {
   v4u a;
