@@ -8,8 +8,9 @@ One step is one pass of the whole hot path over one batch of synthetic input:
                                        INT4 codes carried as BF6 on the FP6 matrix units)
   kv_int8_quant + kv_int8_dequant      on K and V bf16 [10240 tokens, 32 heads, 128 dim]
 Weight preparation (smoothing, SVD, residual packing) is offline and untimed.  The INT8-unit
-route (svdq_quantize_act + svdq_w4a4_gemm, same codes and result) is timed after the timed
-region and reported beside it.
+route (svdq_quantize_act + svdq_w4a4_gemm, same codes and result) and the W4A8 variant
+(svdq_quantize_act_a8 + svdq_w4a8_gemm: 8-bit activation codes, same INT4 weights) are timed
+after the timed region and reported beside it.
 
 Timing: W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every call
 is bracketed by HIP events on the stream it is launched on, so each kernel's mean duration is
@@ -215,11 +216,9 @@ def main():
     xq4 = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
     xs4 = torch.empty(K // 64, M, dtype=torch.float16, device=dev)
     T4 = torch.empty(M, RANK, dtype=torch.float32, device=dev)
-    int8_ms = {}
-    for name, fn in (("act", lambda: B.svdq_quantize_act(X[0], pw.inv_lambda, pw.L1t, RANK, xq4,
-                                                          xs4, T4, stream)),
-                     ("gemm", lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2t, None,
-                                                       RANK, Y[0], stream))):
+    xq8 = torch.empty(M, K, dtype=torch.int8, device=dev)   # W4A8 variant: 8-bit activations
+
+    def time10(fn):
         fn()
         torch.cuda.synchronize()
         evs = []
@@ -230,7 +229,20 @@ def main():
             e1.record(stream)
             evs.append((e0, e1))
         torch.cuda.synchronize()
-        int8_ms[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    int8_ms = {
+        "act": time10(lambda: B.svdq_quantize_act(X[0], pw.inv_lambda, pw.L1t, RANK, xq4, xs4,
+                                                  T4, stream)),
+        "gemm": time10(lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
+                                                stream)),
+    }
+    w4a8_ms = {
+        "act": time10(lambda: B.svdq_quantize_act_a8(X[0], pw.inv_lambda, pw.L1t, RANK, xq8, xs4,
+                                                     T4, stream)),
+        "gemm": time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
+                                                stream)),
+    }
     gemm_ops = 2.0 * M * N * K
     gemm_tops = gemm_ops / (ms["gemm"] * 1e-3) / 1e12
     ab = algorithmic_bytes()
@@ -272,6 +284,10 @@ def main():
         "int8_route": {"gemm_ms": round(int8_ms["gemm"], 5), "act_ms": round(int8_ms["act"], 5),
                        "gemm_TOPS": round(gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12, 2),
                        "pct_int8_peak": round(100.0 * gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12
+                                              / INT8_PEAK_TOPS, 2)},
+        "w4a8_route": {"gemm_ms": round(w4a8_ms["gemm"], 5), "act_ms": round(w4a8_ms["act"], 5),
+                       "gemm_TOPS": round(gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12, 2),
+                       "pct_int8_peak": round(100.0 * gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12
                                               / INT8_PEAK_TOPS, 2)},
         "setup_s": round(setup_s, 1),
     }

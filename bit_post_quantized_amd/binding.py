@@ -36,6 +36,9 @@ _SIGNATURES = {
     "svdq_quantize_act_e3m2": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "svdq_w4a4_gemm_e3m2": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "svdq_w4a4_partials_e3m2": ([_P, _P, _I, _I, _I, _P, _P], _I),
+    "svdq_quantize_act_a8": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
+    "svdq_w4a8_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
+    "svdq_w4a8_partials": ([_P, _P, _I, _I, _I, _P, _P], _I),
     "kv_int8_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "kv_int8_quant": ([_P, _I, _I, _P, _P, _P, _P, _P], _I),
     "kv_int8_dequant": ([_P, _P, _P, _I, _I, _P, _P], _I),
@@ -198,3 +201,35 @@ def kv_int8_dequant(q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
     channels = q.numel() // tokens if tokens else int(torch.tensor(q.shape[1:]).prod())
     _check("kv_int8_dequant", load().kv_int8_dequant(
         _ptr(q), _ptr(scale), _ptr(zero), tokens, channels, _ptr(x_out), _stream(stream)))
+
+
+def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[torch.Tensor],
+                         r: int, xq8: torch.Tensor, x_scales: torch.Tensor,
+                         T: Optional[torch.Tensor], stream=None) -> None:
+    """W4A8 activation pass: X bf16 [M, K] -> xq8 int8 [M, K], x_scales fp16 [K/64, M],
+    T fp32 [M, r]."""
+    M, K = X.shape
+    _check("svdq_quantize_act_a8", load().svdq_quantize_act_a8(
+        _ptr(X), _ptr(inv_lambda), _ptr(L1), M, K, r, _ptr(xq8), _ptr(x_scales), _ptr(T),
+        _stream(stream)))
+
+
+def svdq_w4a8_gemm(xq8: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
+                   wq: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
+                   bias: Optional[torch.Tensor], r: int, Y: torch.Tensor, stream=None) -> None:
+    """Y [M, N] of the W4A8 GEMM: int8 activation codes xq8 [M, K], INT4 nibbles wq [N, K/2]."""
+    M, K = xq8.shape
+    N = wq.shape[0]
+    out = SVDQ_OUT_FP32 if Y.dtype == torch.float32 else SVDQ_OUT_BF16
+    _check("svdq_w4a8_gemm", load().svdq_w4a8_gemm(
+        _ptr(xq8), _ptr(x_scales), _ptr(T), _ptr(wq), _ptr(w_scales), _ptr(L2), _ptr(bias),
+        M, N, K, r, _ptr(Y), out, _stream(stream)))
+
+
+def svdq_w4a8_partials(xq8: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
+                       stream=None) -> None:
+    """P int32 [K/64, M, N]: the exact group partials of the W4A8 GEMM's inner loop."""
+    M, K = xq8.shape
+    N = wq.shape[0]
+    _check("svdq_w4a8_partials", load().svdq_w4a8_partials(
+        _ptr(xq8), _ptr(wq), M, N, K, _ptr(P), _stream(stream)))

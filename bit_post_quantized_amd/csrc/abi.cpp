@@ -95,7 +95,7 @@ int svdq_pack_weights_e3m2(const float* R, int K, int N, uint8_t* wq6, uint16_t*
 
 static int quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
                         int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream,
-                        int e3m2, const char* name) {
+                        int codes, const char* name) {
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0 (got %d)", M);
   if (int s = check_k(K)) return s;
   if (int s = check_rank(r)) return s;
@@ -105,22 +105,28 @@ static int quantize_act(const uint16_t* X, const float* inv_lambda, const uint16
   if (!aligned16(X) || !aligned16(inv_lambda) || !aligned16(xq) || (r > 0 && !aligned16(L1)))
     return fail(SVDQ_EALIGN, "X, inv_lambda, xq and L1 must be 16-byte aligned");
   if (M == 0) return ok();
-  return hip_status(svdq::launch_quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, e3m2,
+  return hip_status(svdq::launch_quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, codes,
                                               (hipStream_t)stream),
                     name);
 }
 
 int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
                       int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream) {
-  return quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream, 0,
+  return quantize_act(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream, svdq::kCodesNibbles,
                       "svdq_quantize_act");
 }
 
 int svdq_quantize_act_e3m2(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                            int M, int K, int r, uint8_t* xq6, uint16_t* x_scales, float* T,
                            void* stream) {
-  return quantize_act(X, inv_lambda, L1, M, K, r, xq6, x_scales, T, stream, 1,
+  return quantize_act(X, inv_lambda, L1, M, K, r, xq6, x_scales, T, stream, svdq::kCodesBf6,
                       "svdq_quantize_act_e3m2");
+}
+
+int svdq_quantize_act_a8(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                         int K, int r, int8_t* xq8, uint16_t* x_scales, float* T, void* stream) {
+  return quantize_act(X, inv_lambda, L1, M, K, r, reinterpret_cast<uint8_t*>(xq8), x_scales, T,
+                      stream, svdq::kCodesInt8, "svdq_quantize_act_a8");
 }
 
 static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K) {
@@ -198,6 +204,20 @@ int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N
                             int32_t* P, void* stream) {
   return partials(svdq::launch_w4a4_gemm_e3m2, "svdq_w4a4_partials_e3m2", xq6, wq6, M, N, K, P,
                   stream);
+}
+
+int svdq_w4a8_gemm(const int8_t* xq8, const uint16_t* x_scales, const float* T,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
+                   void* stream) {
+  return gemm(svdq::launch_w4a8_gemm, "svdq_w4a8_gemm", reinterpret_cast<const uint8_t*>(xq8),
+              x_scales, T, wq, w_scales, L2, bias, M, N, K, r, Y, out_dtype, stream);
+}
+
+int svdq_w4a8_partials(const int8_t* xq8, const uint8_t* wq, int M, int N, int K, int32_t* P,
+                       void* stream) {
+  return partials(svdq::launch_w4a8_gemm, "svdq_w4a8_partials",
+                  reinterpret_cast<const uint8_t*>(xq8), wq, M, N, K, P, stream);
 }
 
 size_t kv_int8_workspace_bytes(int tokens, int channels) {

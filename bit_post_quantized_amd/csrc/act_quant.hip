@@ -1,22 +1,23 @@
-// Fused activation pass: smoothing, dynamic INT4 quantization and the low-rank down-projection.
+// Fused activation pass: smoothing, dynamic low-bit quantization and the low-rank
+// down-projection.
 //
 // SVDQ "technical principles": smoothing moves activation outliers into the weights, and a
 // 16-bit low-rank branch runs beside the 4-bit one.  FLUX4 3.1: activations are quantized at
-// run time.  W4A8 3.1: symmetric scale max|v| / (2^(b-1) - 1), round, clamp (b = 4 here, one
-// scale per token and 64-group).  SVDQ / DCMP: the branch is fused so the activations are read
-// from HBM once.
+// run time.  W4A8 3.1: symmetric scale max|v| / (2^(b-1) - 1), round, clamp, one scale per
+// token and 64-group; b = 4 (INT4 codes) or b = 8 (the W4A8 variant's activations, W4A8 1).
+// SVDQ / DCMP: the branch is fused so the activations are read from HBM once.
 //
 // Work decomposition.  A workgroup owns 16 tokens (rows) and all of K; its waves take the
 // 64-groups round-robin.  In a group, lane l holds row l % 16 and the 16 consecutive k
 // [16 q, 16 q + 16) of quarter q = l / 16: two 16-byte loads, so every load instruction reads
 // 16 rows x 64 contiguous bytes.  The loads of kActBatch groups are issued before any of them is
-// used.  The group max is folded over the four quarter lanes of a row with two lane shuffles;
-// every lane then codes its 16 values (exact quotient, no division per element) and writes
-// them as 8 bytes of nibbles, or as 12 bytes of BF6 (E3M2) codes into the tiled container (its
-// row block, group, slot row % 32 + 32 (q / 2), byte 12 (q % 2)) -- the two containers the GEMMs
-// read -- and the quarter-0 lanes write the 16 rows' scales (32 contiguous bytes).  For the
-// tiled container the grid also covers the rows up to the next multiple of 32, whose codes it
-// writes as zeros.
+// used; inv_lambda sits in LDS.  The group max is folded over the four quarter lanes of a row
+// with two lane shuffles; every lane then codes its 16 values (exact quotient, no division per
+// element) as biased bytes c + 2^(b-1) and writes them in one of three containers: 8 bytes of
+// nibbles, 12 bytes of BF6 (E3M2) patterns into the tiled container (its row block, group,
+// slot row % 32 + 32 (q / 2), byte 12 (q % 2)), or 16 bytes of int8.  The quarter-0 lanes write
+// the 16 rows' scales.  For the tiled container the grid also covers the rows up to the next
+// multiple of 32, whose codes it writes as zeros.
 // Low-rank branch: the same registers rounded to bf16 are the A operand of two
 // v_mfma_f32_16x16x32_bf16 per group (k-slots 8 (l / 16) + i of the MFMA take k = 16 q + i and
 // 16 q + 8 + i), and L1, stored K-contiguous, is loaded with the same k map, so the MFMAs sum
@@ -32,7 +33,8 @@ constexpr int kActBatch = 6;    // groups per wave whose code loads are in fligh
 constexpr int kActMaxWaves = 8;
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
-template <int NTR, bool E3M2, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
+// CODES: kCodesNibbles, kCodesBf6 (INT4 codes) or kCodesInt8 (8-bit codes of the W4A8 variant)
+template <int NTR, int CODES, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
 __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
@@ -133,31 +135,36 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
       for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-      const uint16_t sb = int4_scale_bits(amax);
+      constexpr bool I8 = CODES == kCodesInt8;
+      const uint16_t sb = I8 ? float_to_half_bits(amax / 127.0f) : int4_scale_bits(amax);
       const float s = half_bits_to_float(sb);
       const float s1 = s == 0.0f ? 1.0f : s;  // an all-zero group: every quotient is 0
       const bool live = row < M;
       // padding rows get 1 / s = 0: every quotient is then exactly 0, so no select per code
       const float rcp = live ? 1.0f / s1 : 0.0f;
-      // code + 8 as bytes: rne of the correctly rounded quotient, + 8, clamp to [0, 15]
-      // (a -0 quotient becomes +8 here, so both zeros give the code 0)
+      // code + 8 (+ 128 for 8-bit codes) as bytes: rne of the correctly rounded quotient, the
+      // bias, clamp to [0, 15] ([0, 255]); a -0 quotient becomes the bias, so both zeros give 0
+      constexpr float kBias = I8 ? 128.0f : 8.0f, kTop = I8 ? 255.0f : 15.0f;
       uint32_t bq[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[4 * d + i], s1, rcp) + 8.0f, 0.0f, 15.0f);
+          v[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[4 * d + i], s1, rcp) + kBias, 0.0f, kTop);
         bq[d] = bytes4(v);
       }
       if (gv) {
-        if constexpr (E3M2) {  // rows up to the block boundary (padding rows get zero codes)
+        if constexpr (CODES == kCodesBf6) {  // rows up to the block boundary (padding rows: zero codes)
           uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
           *reinterpret_cast<v3u*>(dst) = pack16_bf6_biased(bq);
         }
         if (live) {
-          if constexpr (!E3M2)
+          if constexpr (CODES == kCodesNibbles)
             *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{nibbles8_biased(bq[0], bq[1]), nibbles8_biased(bq[2], bq[3])};
+          if constexpr (I8)  // c + 128 xor 128 is the two's complement byte of c
+            *reinterpret_cast<v4u*>(xq + (size_t)row * K + (size_t)g * kGroup + 16 * q) =
+                v4u{bq[0], bq[1], bq[2], bq[3]} ^ 0x80808080u;
           if (q == 0) x_scales[(size_t)g * M + row] = sb;
         }
       }
@@ -192,22 +199,22 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
   }
 }
 
-template <bool E3M2, bool LAM_LDS>
+template <int CODES, bool LAM_LDS>
 static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                              int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                              int nwaves, size_t lds, hipStream_t stream) {
   // the tiled BF6 container is written up to the next multiple of 32 rows
-  const int rows = E3M2 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
+  const int rows = CODES == kCodesBf6 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
   const dim3 grid((rows + kActRows - 1) / kActRows), block(64 * nwaves);
   switch (r / 16) {
 #define SVDQ_ACT_CASE(n)                                                                   \
   case n: {                                                                                \
-    const void* fn = reinterpret_cast<const void*>(quantize_act_kernel<n, E3M2, LAM_LDS>);  \
+    const void* fn = reinterpret_cast<const void*>(quantize_act_kernel<n, CODES, LAM_LDS>);  \
     if (lds > 64 * 1024) {                                                                 \
       const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e != hipSuccess) return e;                                                       \
     }                                                                                      \
-    hipLaunchKernelGGL((quantize_act_kernel<n, E3M2, LAM_LDS>), grid, block, lds, stream, X, \
+    hipLaunchKernelGGL((quantize_act_kernel<n, CODES, LAM_LDS>), grid, block, lds, stream, X, \
                        inv_lambda, L1, M, K, xq, x_scales, T);                             \
     break;                                                                                 \
   }
@@ -227,7 +234,7 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
   return hipGetLastError();
 }
 
-template <bool E3M2>
+template <int CODES>
 static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                    int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                                    hipStream_t stream) {
@@ -236,15 +243,23 @@ static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, c
   const size_t red = (size_t)nwaves * 16 * r * sizeof(float);
   const size_t lam = (size_t)K * sizeof(float);
   if (lam + red <= kActLdsLambda)
-    return launch_act<E3M2, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red, stream);
-  return launch_act<E3M2, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, stream);
+    return launch_act<CODES, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red, stream);
+  return launch_act<CODES, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, stream);
 }
 
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                               int e3m2, hipStream_t stream) {
-  return e3m2 ? launch_act_route<true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream)
-              : launch_act_route<false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
+                               int codes, hipStream_t stream) {
+  switch (codes) {
+    case kCodesNibbles:
+      return launch_act_route<kCodesNibbles>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
+    case kCodesBf6:
+      return launch_act_route<kCodesBf6>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
+    case kCodesInt8:
+      return launch_act_route<kCodesInt8>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace svdq

@@ -8,15 +8,25 @@
 
 namespace svdq {
 
-// e3m2 != 0: write the codes as BF6 (E3M2) records [rows, 3K/4] instead of nibbles [rows, K/2]
+// e3m2 != 0: write the codes into the tiled BF6 container instead of nibbles [rows, K/2]
 hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_scales,
                                int e3m2, hipStream_t stream);
 
+// code containers of the activation pass: INT4 as nibbles [M, K/2], INT4 as the tiled BF6
+// container, or the 8-bit codes of the W4A8 variant [M, K] (int8)
+constexpr int kCodesNibbles = 0, kCodesBf6 = 1, kCodesInt8 = 2;
+
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                               int e3m2, hipStream_t stream);
+                               int codes, hipStream_t stream);
 
 hipError_t launch_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
+                            const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                            const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                            int out_fp32, int32_t* partials, hipStream_t stream);
+
+// W4A8: int8 activation codes [M, K] times the INT4 weight nibbles, on the INT8 matrix units
+hipError_t launch_w4a8_gemm(const uint8_t* xq8, const uint16_t* x_scales, const float* T,
                             const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
                             const uint16_t* bias, int M, int N, int K, int r, void* Y,
                             int out_fp32, int32_t* partials, hipStream_t stream);

@@ -22,6 +22,10 @@
 //    lanes 0..15 keep the fp16 scale they read from LDS, lanes 16..63 zero it.
 //    The dequantization is then one convert and one FMA per output and group.  The factor 256
 //    of the unpacked operands is removed once, exactly, in the epilogue.
+//  * W4A8 variant (A8): the activation operand arrives as 8-bit codes (W4A8 1, 2.2: 8-bit
+//    activations, 4-bit weights widened onto the INT8 units).  Its 16-byte segments are only
+//    reordered, with two v_perm_b32 per 8 codes, into the k order the weights' unpack gives;
+//    the products then carry 16 (the weights' pre-shift) instead of 256.
 //  * Epilogue.  bf16(T) [16 x 32] and L2 [32 x 16] fragments go through
 //    v_mfma_f32_16x16x32_bf16 with the fp32 accumulator as C, then the bias is added and the
 //    tile is rounded to bf16 (or kept fp32) and stored.
@@ -54,7 +58,8 @@ struct GemmTile {
 
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 
-template <class TL, bool OUT_FP32, bool PARTIALS, int NTR>
+// A8: the activation operand holds 8-bit codes [M, K] (the W4A8 variant) instead of nibbles.
+template <class TL, bool OUT_FP32, bool PARTIALS, int NTR, bool A8 = false>
 __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(TL::WAVES_PER_EU)))
 void w4a4_gemm_kernel(
     const uint8_t* __restrict__ xq, const uint16_t* __restrict__ x_scales,
@@ -77,13 +82,16 @@ void w4a4_gemm_kernel(
 
   // ---- staging: segment s of an operand tile is the 16 packed bytes [16 (s & 1), +16) of row
   //      (or column) s / 2; thread t moves segments t, t + NT, ... of A and of B
-  constexpr int SA_PER = 2 * TM / NT, SB_PER = 2 * TN / NT;
+  //      (8-bit activation codes: a row's group is 64 bytes, four segments of 16 codes)
+  constexpr int ASEG = A8 ? 4 : 2;  // 16-byte segments per row and group
+  constexpr int SA_PER = ASEG * TM / NT, SB_PER = 2 * TN / NT;
   const uint8_t* a_src[SA_PER];
   const uint8_t* b_src[SB_PER];
 #pragma unroll
   for (int u = 0; u < SA_PER; ++u) {
     const int sg = tid + u * NT;
-    a_src[u] = xq + (size_t)min(m_tile + (sg >> 1), M - 1) * ldq + (sg & 1) * 16;
+    a_src[u] = A8 ? xq + (size_t)min(m_tile + (sg >> 2), M - 1) * (size_t)K + (sg & 3) * 16
+                  : xq + (size_t)min(m_tile + (sg >> 1), M - 1) * ldq + (sg & 1) * 16;
   }
 #pragma unroll
   for (int u = 0; u < SB_PER; ++u) {
@@ -110,9 +118,21 @@ void w4a4_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < SA_PER; ++u) {
       const int sg = tid + u * NT;
-      uint8_t* d = st + (sg >> 1) * kRowBytes + (sg & 1) * 32;
-      reinterpret_cast<v4i*>(d)[0] = unpack16_x16(v2u{a[u].x, a[u].y});
-      reinterpret_cast<v4i*>(d)[1] = unpack16_x16(v2u{a[u].z, a[u].w});
+      if constexpr (A8) {
+        // 16 codes k0..k15 in natural order -> the order unpack16_x16 gives the weights
+        // (k0 k2 k4 k6 | k1 k3 k5 k7 | k8 k10 k12 k14 | k9 k11 k13 k15), so both operands of
+        // the MFMA see the same k in every byte slot
+        uint8_t* d = st + (sg >> 2) * kRowBytes + (sg & 3) * 16;
+        const v4u v = a[u];
+        *reinterpret_cast<v4u*>(d) = v4u{__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                                         __builtin_amdgcn_perm(v.y, v.x, 0x07050301u),
+                                         __builtin_amdgcn_perm(v.w, v.z, 0x06040200u),
+                                         __builtin_amdgcn_perm(v.w, v.z, 0x07050301u)};
+      } else {
+        uint8_t* d = st + (sg >> 1) * kRowBytes + (sg & 1) * 32;
+        reinterpret_cast<v4i*>(d)[0] = unpack16_x16(v2u{a[u].x, a[u].y});
+        reinterpret_cast<v4i*>(d)[1] = unpack16_x16(v2u{a[u].z, a[u].w});
+      }
     }
 #pragma unroll
     for (int u = 0; u < SB_PER; ++u) {
@@ -148,7 +168,7 @@ void w4a4_gemm_kernel(
   uint16_t rs[PD][SS_PER];
   auto load_group = [&](int gg, v4u* a, v4u* b, uint16_t* sc) {
 #pragma unroll
-    for (int u = 0; u < SA_PER; ++u) a[u] = *reinterpret_cast<const v4u*>(a_src[u] + (size_t)gg * 32);
+    for (int u = 0; u < SA_PER; ++u) a[u] = *reinterpret_cast<const v4u*>(a_src[u] + (size_t)gg * (A8 ? 64 : 32));
 #pragma unroll
     for (int u = 0; u < SB_PER; ++u) b[u] = *reinterpret_cast<const v4u*>(b_src[u] + (size_t)gg * 32);
 #pragma unroll
@@ -185,7 +205,7 @@ void w4a4_gemm_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = m_tile + wm * WM + 16 * i + 4 * kc + e;
-            if (row < M && col < N) P[((size_t)g * M + row) * N + col] = p[e] >> 8;  // exact
+            if (row < M && col < N) P[((size_t)g * M + row) * N + col] = p[e] >> (A8 ? 4 : 8);  // exact
           }
         }
       } else {
@@ -221,11 +241,12 @@ void w4a4_gemm_kernel(
   }
   if constexpr (PARTIALS) return;
 
-  // ---- epilogue: remove the 256 of the unpacked operands, low-rank up-projection, bias
+  // ---- epilogue: remove the 256 of the unpacked operands (16 with 8-bit activation codes,
+  //      whose operand is not pre-shifted), low-rank up-projection, bias
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] *= 0x1p-8f;
+    for (int j = 0; j < FN; ++j) acc[i][j] *= A8 ? 0x1p-4f : 0x1p-8f;
   // The epilogue's addresses are loop-invariant; computed before the K loop they would stay
   // live across it and spill.  An opaque copy of the indices keeps them here.
   int row0 = m_tile + wm * WM, col0 = n_tile + wn * WN, Mo = M, No = N;
@@ -278,17 +299,19 @@ void w4a4_gemm_kernel(
   }
 }
 
-// Tile used for every launch (see the design notes at the top of the file).
-using Tile = GemmTile<128, 128, 64, 64, 2, 3>;
+// Tile used for every launch (see the design notes at the top of the file).  A register
+// prefetch ring of one group: two groups (or the W4A8 variant's twice larger activation
+// segments) spill at this occupancy and measured slower.
+using Tile = GemmTile<128, 128, 64, 64, 1, 3>;
 
 // The double-buffered stage may need more than the default 64 KB of dynamic LDS.
 template <typename F>
-static hipError_t allow_lds(F kernel) {
+static hipError_t allow_lds(F kernel, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile::kLdsBytes);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <bool OUT_FP32, bool PARTIALS>
+template <bool OUT_FP32, bool PARTIALS, bool A8 = false>
 static hipError_t launch_ntr(int ntr, dim3 grid, hipStream_t stream, const uint8_t* xq,
                              const uint16_t* x_scales, const float* T, const uint8_t* wq,
                              const uint16_t* w_scales, const uint16_t* L2, const uint16_t* bias,
@@ -296,9 +319,10 @@ static hipError_t launch_ntr(int ntr, dim3 grid, hipStream_t stream, const uint8
   switch (ntr) {
 #define SVDQ_GEMM_CASE(n)                                                                       \
   case n: {                                                                                     \
-    const hipError_t e = allow_lds(w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n>);              \
+    const hipError_t e = allow_lds(w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n, A8>,            \
+                                   Tile::kLdsBytes);                                            \
     if (e != hipSuccess) return e;                                                              \
-    hipLaunchKernelGGL((w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n>), grid,                   \
+    hipLaunchKernelGGL((w4a4_gemm_kernel<Tile, OUT_FP32, PARTIALS, n, A8>), grid,               \
                        dim3(Tile::THREADS), Tile::kLdsBytes, stream, xq, x_scales, T, wq,       \
                        w_scales, L2, bias, M, N, K, Y, P);                                      \
     break;                                                                                      \
@@ -332,6 +356,21 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const f
                                    M, N, K, Y, nullptr);
   return launch_ntr<false, false>(r / 16, grid, stream, xq, x_scales, T, wq, w_scales, L2, bias,
                                   M, N, K, Y, nullptr);
+}
+
+hipError_t launch_w4a8_gemm(const uint8_t* xq8, const uint16_t* x_scales, const float* T,
+                            const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                            const uint16_t* bias, int M, int N, int K, int r, void* Y,
+                            int out_fp32, int32_t* partials, hipStream_t stream) {
+  dim3 grid((N + Tile::TN - 1) / Tile::TN, (M + Tile::TM - 1) / Tile::TM);
+  if (partials)
+    return launch_ntr<false, true, true>(0, grid, stream, xq8, nullptr, nullptr, wq, nullptr,
+                                         nullptr, nullptr, M, N, K, nullptr, partials);
+  if (out_fp32)
+    return launch_ntr<true, false, true>(r / 16, grid, stream, xq8, x_scales, T, wq, w_scales,
+                                         L2, bias, M, N, K, Y, nullptr);
+  return launch_ntr<false, false, true>(r / 16, grid, stream, xq8, x_scales, T, wq, w_scales, L2,
+                                        bias, M, N, K, Y, nullptr);
 }
 
 }  // namespace svdq

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 2
+#define SVDQ_ABI_VERSION 3
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -154,10 +154,38 @@ int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N
                             int32_t* P, void* stream);
 
 /*
+ * W4A8 variant (W4A8 sections 1, 3.1, 2.2: 8-bit activations, 4-bit weights widened to 8 bits
+ * on the INT8 units).  The activation codes are 8-bit, per (token, 64-group):
+ *     s = fp16(fl32(amax / 127)),  q = clamp(rne(fl32(x^ / s)), -128, 127),  q = 0 when s == 0,
+ * with the smoothing and the low-rank down-projection T of svdq_quantize_act; the weights are
+ * those of svdq_pack_weights (INT4 nibbles), and
+ *     Y[m, n] = sum_g s_x[g, m] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
+ *     P[g, m, n] = sum_{k in group g} q8x[m, k] qw[n, k]   (exact int32).
+ * svdq_quantize_act_a8 — svdq_quantize_act writing xq8, int8 [M, K] (two's complement, one code
+ *   per byte, 16B) instead of nibbles.
+ * svdq_w4a8_gemm — svdq_w4a4_gemm reading xq8 instead of xq.
+ * svdq_w4a8_partials — test entry: the exact group partials of the same device inner loop as
+ *   svdq_w4a8_gemm, P int32 [G, M, N].
+ * Arguments, shapes, alignment and error behaviour are otherwise those of the matching W4A4
+ * entry point.
+ */
+int svdq_quantize_act_a8(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+                         int K, int r, int8_t* xq8, uint16_t* x_scales, float* T, void* stream);
+int svdq_w4a8_gemm(const int8_t* xq8, const uint16_t* x_scales, const float* T,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
+                   void* stream);
+int svdq_w4a8_partials(const int8_t* xq8, const uint8_t* wq, int M, int N, int K, int32_t* P,
+                       void* stream);
+
+/*
  * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its
- * cross-token min/max reduction: one partial (lo, hi) per channel and 64-token chunk (0 when
- * tokens == 0).  Its contents need no initialization and carry nothing between calls; calls
- * that share one workspace must not overlap in time (one stream, or one workspace per stream).
+ * cross-token min/max reduction (0 when tokens == 0): the per-part partial ranges and tags of
+ * the single-pass schedule, or the per-64-token-chunk partials of the three-pass schedule for
+ * shapes the single pass does not take; the size covers either.  Its contents need no
+ * initialization and carry nothing between calls (a tag left by an earlier call never matches
+ * a later one); calls that share one workspace must not overlap in time (one stream, or one
+ * workspace per stream).
  */
 size_t kv_int8_workspace_bytes(int tokens, int channels);
 

@@ -100,23 +100,26 @@ def attach_lora(L1b, L2b, lam32, A, B, scale: float = 1.0):
 
 
 # --------------------------------------------------------------------------- 4-bit quantizer
-def quantize_groups(V32: np.ndarray):
-    """Symmetric INT4 quantization of each length-64 vector along the last axis
+def quantize_groups(V32: np.ndarray, bits: int = 4):
+    """Symmetric b-bit quantization of each length-64 vector along the last axis
     (W4A8 3.1 "quantization process": scale from the max magnitude over 2^(b-1)-1, round,
-    clamp to the b-bit range; here b = 4).
+    clamp to the b-bit range).  b = 4 for the W4A4 path; b = 8 for the activations of the
+    W4A8 variant.
 
     V32: float32 [..., 64]. Returns (codes int8 [..., 64], scales float16 [...]).
     """
+    qmax = 2 ** (bits - 1) - 1
+    qmin = -(2 ** (bits - 1))
     V32 = np.asarray(V32, dtype=np.float32)
     assert V32.shape[-1] == GROUP
     amax = np.max(np.abs(V32), axis=-1)
-    s16 = round_fp16(amax / np.float32(7.0))
+    s16 = round_fp16(amax / np.float32(qmax))
     if np.any(np.isinf(s16)):
-        raise ValueError("group max / 7 exceeds the fp16 range (outside the contract)")
+        raise ValueError(f"group max / {qmax} exceeds the fp16 range (outside the contract)")
     s32 = s16.astype(np.float32)
     zero = s32 == 0
     quot = V32 / np.where(zero, np.float32(1.0), s32)[..., None]
-    q = np.clip(np.rint(quot), QMIN, QMAX).astype(np.int8)
+    q = np.clip(np.rint(quot), qmin, qmax).astype(np.int8)
     q[zero] = 0
     return q, s16
 
@@ -267,12 +270,29 @@ def quantize_act(X_bits, inv_lam32, L1b) -> dict:
     return dict(xq=pack_nibbles(codes), s_x=s16, codes=codes, X_hat=Xh, T=T)
 
 
+def quantize_act_a8(X_bits, inv_lam32, L1b) -> dict:
+    """W4A8 variant of the activation pass (W4A8 1, 3.1: 8-bit activations, integers in
+    [-128, 127], scale = max|v| / 127 per (token, 64-group)); smoothing and the low-rank
+    down-projection are those of ``quantize_act``.  Returns codes int8 [M, K] (also the
+    stored layout), s_x float16 [M, G], T."""
+    Xh = smooth_activations(X_bits, inv_lam32)
+    M, K = Xh.shape
+    G = K // GROUP
+    q, s16 = quantize_groups(Xh.reshape(M, G, GROUP), bits=8)
+    codes = q.reshape(M, K)
+    T = None
+    if L1b is not None and np.asarray(L1b).shape[1] > 0:
+        T = Xh.astype(np.float64) @ np.asarray(L1b, dtype=np.float64)
+    return dict(xq8=codes.copy(), s_x=s16, codes=codes, X_hat=Xh, T=T)
+
+
 # --------------------------------------------------------------------------- integer GEMM
 def int_partials(cx: np.ndarray, cw: np.ndarray) -> np.ndarray:
     """P[g, m, n] = sum_{k in group g} cx[m, k] cw[n, k] (cx [M, K], cw [N, K] int codes).
 
     Evaluated with fp64 matrix products on integer-valued matrices: every product and partial
-    sum is an integer of magnitude <= 64 * 64, far below 2^53, so the result is exact.
+    sum is an integer of magnitude <= 64 * 128 * 8 (8-bit activation codes included), far below
+    2^53, so the result is exact.
     """
     M, K = cx.shape
     N = cw.shape[0]

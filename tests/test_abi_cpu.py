@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 2
+    assert lib.svdq_abi_version() == 3
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -107,10 +107,31 @@ def test_e3m2_entry_points_validate_like_their_nibble_twins(lib):
     assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
 
 
+def test_w4a8_entry_points_validate_like_their_w4a4_twins(lib):
+    f = lib.svdq_quantize_act_a8
+    assert f(FAKE, FAKE, FAKE, 4, 128, 20, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, FAKE, 4, 96, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(FAKE, FAKE, None, 4, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, FAKE, FAKE, 4, 128, 16, ODD, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    assert f(FAKE, FAKE, FAKE, 0, 128, 16, FAKE, FAKE, FAKE, None) == binding.SVDQ_OK
+    g = lib.svdq_w4a8_gemm
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert g(*args, 8, 8, 100, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert g(*args, 8, 0, 128, 0, FAKE, 0, None) == binding.SVDQ_EINVAL
+    assert g(*args, 8, 8, 128, 0, FAKE, 7, None) == binding.SVDQ_EINVAL
+    assert g(ODD, FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, 8, 128, 0, FAKE, 0, None) == binding.SVDQ_EALIGN
+    assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK
+    p = lib.svdq_w4a8_partials
+    assert p(FAKE, FAKE, 8, 8, 96, FAKE, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, FAKE, 8, 8, 128, None, None) == binding.SVDQ_EINVAL
+    lib.svdq_w4a8_partials(FAKE, FAKE, 8, 8, 96, FAKE, None)
+    assert b"multiple of 64" in lib.svdq_last_error()
+
+
 def test_kv_validation(lib):
     q = lib.kv_int8_quant
     assert lib.kv_int8_workspace_bytes(0, 4096) == 0
-    # lo/hi partials of 160 chunks of 64 tokens
+    # the larger of the two schedules' needs: lo/hi partials of 160 chunks of 64 tokens
     assert lib.kv_int8_workspace_bytes(10240, 4096) == 2 * 160 * 4096 * 4
     assert q(FAKE, 16, 12, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
     assert q(FAKE, -1, 16, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_EINVAL
