@@ -10,7 +10,8 @@ One step is one pass of the whole hot path over one batch of synthetic input:
 Weight preparation (smoothing, SVD, residual packing) is offline and untimed.  The INT8-unit
 route (svdq_quantize_act + svdq_w4a4_gemm, same codes and result) and the W4A8 variant
 (svdq_quantize_act_a8 + svdq_w4a8_gemm: 8-bit activation codes, same INT4 weights) are timed
-after the timed region and reported beside it.
+after the timed region and reported beside it, and so is kv_int8_attention (decode attention
+of one query per head reading the INT8 K and V codes of one batch).
 
 Timing: W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every call
 is bracketed by HIP events on the stream it is launched on, so each kernel's mean duration is
@@ -243,6 +244,15 @@ def main():
         "gemm": time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
                                                 stream)),
     }
+    # decode attention over the INT8 cache of batch 0 (one query per head): reads the codes
+    q_att = torch.randn(1, KV_H, KV_D, device=dev).to(torch.bfloat16)
+    o_att = torch.empty(1, KV_H, KV_D, dtype=torch.bfloat16, device=dev)
+    ws_att = torch.empty(B.kv_int8_attention_workspace_bytes(1, KV_T, KV_H, KV_D),
+                         dtype=torch.uint8, device=dev)
+    attn_ms = time10(lambda: B.kv_int8_attention(q_att, q[0][0], sc[0][0], zp[0][0], q[0][1],
+                                                 sc[0][1], zp[0][1], KV_D ** -0.5, o_att, ws_att,
+                                                 stream))
+    attn_bytes = 2 * KV_T * C + 2 * C * 5 + 2 * 1 * C * 2
     gemm_ops = 2.0 * M * N * K
     gemm_tops = gemm_ops / (ms["gemm"] * 1e-3) / 1e12
     ab = algorithmic_bytes()
@@ -289,6 +299,10 @@ def main():
                        "gemm_TOPS": round(gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12, 2),
                        "pct_int8_peak": round(100.0 * gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12
                                               / INT8_PEAK_TOPS, 2)},
+        "kv_attention": {"ms": round(attn_ms, 5), "queries": 1,
+                         "GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+                         "pct_hbm_peak": round(100.0 * attn_bytes / (attn_ms * 1e-3) / 1e9
+                                               / HBM_PEAK_GBPS, 2)},
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out))

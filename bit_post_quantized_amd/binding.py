@@ -42,6 +42,9 @@ _SIGNATURES = {
     "kv_int8_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "kv_int8_quant": ([_P, _I, _I, _P, _P, _P, _P, _P], _I),
     "kv_int8_dequant": ([_P, _P, _P, _I, _I, _P, _P], _I),
+    "kv_int8_attention_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "kv_int8_attention": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P,
+                           _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -233,3 +236,21 @@ def svdq_w4a8_partials(xq8: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
     N = wq.shape[0]
     _check("svdq_w4a8_partials", load().svdq_w4a8_partials(
         _ptr(xq8), _ptr(wq), M, N, K, _ptr(P), _stream(stream)))
+
+
+def kv_int8_attention_workspace_bytes(nq: int, tokens: int, heads: int, dim: int) -> int:
+    return load().kv_int8_attention_workspace_bytes(nq, tokens, heads, dim)
+
+
+def kv_int8_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scale: torch.Tensor,
+                      k_zero: torch.Tensor, v_codes: torch.Tensor, v_scale: torch.Tensor,
+                      v_zero: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                      workspace: torch.Tensor, stream=None) -> None:
+    """Decode attention over the INT8 cache: q bf16 [nq, heads, dim], codes uint8
+    [tokens, heads * dim], per-channel scale / zero -> out bf16 [nq, heads, dim]."""
+    nq, heads, dim = q.shape
+    tokens = k_codes.shape[0]
+    _check("kv_int8_attention", load().kv_int8_attention(
+        _ptr(q), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
+        _ptr(v_zero), nq, tokens, heads, dim, float(sm_scale), _ptr(out), _ptr(workspace),
+        _stream(stream)))

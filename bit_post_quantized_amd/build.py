@@ -25,7 +25,7 @@ OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
 SOURCES = ["abi.cpp", "pack_weights.hip", "act_quant.hip", "w4a4_gemm.hip", "w4a4_gemm_e3m2.hip",
-           "kv_int8.hip"]
+           "kv_int8.hip", "kv_attention.hip"]
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

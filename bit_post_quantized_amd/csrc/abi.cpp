@@ -259,4 +259,33 @@ int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, i
                     "kv_int8_dequant");
 }
 
+size_t kv_int8_attention_workspace_bytes(int nq, int tokens, int heads, int dim) {
+  return svdq::kv_attn_workspace_bytes(nq, tokens, heads, dim);
+}
+
+int kv_int8_attention(const uint16_t* q, const uint8_t* k_codes, const float* k_scale,
+                      const uint8_t* k_zero, const uint8_t* v_codes, const float* v_scale,
+                      const uint8_t* v_zero, int nq, int tokens, int heads, int dim,
+                      float sm_scale, uint16_t* out, void* workspace, void* stream) {
+  if (nq <= 0 || tokens <= 0 || heads <= 0)
+    return fail(SVDQ_EINVAL, "nq, tokens and heads must be positive (got %d, %d, %d)", nq, tokens,
+                heads);
+  if (dim != 64 && dim != 128) return fail(SVDQ_ESHAPE, "dim must be 64 or 128 (got %d)", dim);
+  if ((long long)tokens * heads * dim > kMaxElems || nq > 65535 || heads > 65535 ||
+      (tokens + 255) / 256 > 4096)
+    return fail(SVDQ_ESHAPE, "problem too large (at most 1048576 tokens)");
+  if (!q || !k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero || !out ||
+      !workspace)
+    return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
+      !aligned16(k_zero) || !aligned16(workspace))
+    return fail(SVDQ_EALIGN, "q, codes, k_scale, k_zero and workspace must be 16-byte aligned");
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f)
+    return fail(SVDQ_EINVAL, "sm_scale must be finite");
+  return hip_status(svdq::launch_kv_attention(q, k_codes, k_scale, k_zero, v_codes, v_scale,
+                                              v_zero, nq, tokens, heads, dim, sm_scale, out,
+                                              workspace, (hipStream_t)stream),
+                    "kv_int8_attention");
+}
+
 }  // extern "C"

@@ -1,0 +1,228 @@
+// Decode attention that reads the INT8 KV cache directly: the consumer that turns the cache's
+// memory saving into a bandwidth saving (VARC "INT8 KV cache quantization": per-channel codes
+// with a scale and a zero point).
+//
+//     K'[t, c] = (qk[t, c] - zk[c]) sk[c],  V'[t, c] = (qv[t, c] - zv[c]) sv[c],  c = h D + d
+//     out[i, h] = softmax_t(sm_scale q[i, h] . K'[t, h]) V'[t, h]
+//
+// The dequantization is folded out of the token loops.  With q'[c] = q[c] sk[c] sm_scale
+// log2(e) a score is  sum_c q'[c] qk[t, c] - sum_c q'[c] zk[c]  (the second sum is one number
+// per head), in the log2 domain; and sum_t p_t V'[t, c] = sv[c] (sum_t p_t qv[t, c] - zv[c]
+// sum_t p_t), so the value loop accumulates raw codes.  Split over tokens (flash-decoding):
+//  1. kv_attn_partial_kernel: one workgroup per (256-token chunk, head, query).  A thread owns
+//     16 channels of (256 / threads per row) tokens; every K and V code row it needs is loaded
+//     up front (16 bytes per row, 128 contiguous bytes per token and head).  Scores are
+//     reduced over the row's lanes with shuffles, the chunk max and sum over the workgroup,
+//     and the code-space output over tokens in LDS.  It writes (max, sum, O[D]) per chunk.
+//  2. kv_attn_combine_kernel: per (head, query), rescales and sums the chunks' partials and
+//     applies sv, zv; writes bf16.  At most 4096 chunks (1M tokens) per call.
+#include "svdq_device.hpp"
+#include "svdq_launch.hpp"
+
+namespace svdq {
+
+constexpr int kAttnChunk = 256;    // tokens per workgroup
+constexpr int kAttnThreads = 256;
+
+__host__ __device__ inline int attn_chunks(int tokens) { return (tokens + kAttnChunk - 1) / kAttnChunk; }
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void kv_attn_partial_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kq, const float* __restrict__ ks,
+    const uint8_t* __restrict__ kz, const uint8_t* __restrict__ vq, int tokens, int heads,
+    float qscale, float* __restrict__ ws) {
+  constexpr int TPR = D / 16;                 // threads per token row (16 channels each)
+  constexpr int ROWS = kAttnThreads / TPR;    // token rows per pass
+  constexpr int PASSES = kAttnChunk / ROWS;   // token rows per thread
+  __shared__ float red[ROWS][D + 4];
+  __shared__ float wmax[kAttnThreads / 64], wsum[kAttnThreads / 64];
+  const int chunk = blockIdx.x, h = blockIdx.y, qi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lc = tid % TPR, rr = tid / TPR;
+  const int C = heads * D, c0 = h * D + lc * 16;
+
+  // ---- every code row this thread needs, loaded before any is used (rows clamped in range)
+  v4u kr[PASSES], vr[PASSES];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int t = min(chunk * kAttnChunk + rr + ROWS * i, tokens - 1);
+    kr[i] = *reinterpret_cast<const v4u*>(kq + (size_t)t * C + c0);
+    vr[i] = *reinterpret_cast<const v4u*>(vq + (size_t)t * C + c0);
+  }
+
+  // ---- q' = q sk sm_scale log2(e) for this thread's 16 channels, and the zero-point term
+  float qp[16];
+  float zb = 0.0f;
+  {
+    const v4u qw0 = *reinterpret_cast<const v4u*>(q + ((size_t)qi * heads + h) * D + lc * 16);
+    const v4u qw1 = *reinterpret_cast<const v4u*>(q + ((size_t)qi * heads + h) * D + lc * 16 + 8);
+    const uint32_t qwords[8] = {qw0.x, qw0.y, qw0.z, qw0.w, qw1.x, qw1.y, qw1.z, qw1.w};
+    const v4f* sp = reinterpret_cast<const v4f*>(ks + c0);
+    const v4f s4[4] = {sp[0], sp[1], sp[2], sp[3]};
+    const v4u zz = *reinterpret_cast<const v4u*>(kz + c0);
+    const uint32_t zwords[4] = {zz.x, zz.y, zz.z, zz.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = qwords[j >> 1];
+      const float qv = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      qp[j] = qv * s4[j >> 2][j & 3] * qscale;
+      zb = __builtin_fmaf(qp[j], (float)((zwords[j >> 2] >> (8 * (j & 3))) & 0xFFu), zb);
+    }
+  }
+
+  // ---- scores (log2 domain) of this thread's token rows; the row's lanes hold the full sum
+  float sc[PASSES];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+    float a = -zb;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a = __builtin_fmaf(qp[j], (float)((w[j >> 2] >> (8 * (j & 3))) & 0xFFu), a);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) a += __shfl_xor(a, o);
+    const bool valid = chunk * kAttnChunk + rr + ROWS * i < tokens;
+    sc[i] = valid ? a : -__builtin_inff();
+    m = __builtin_fmaxf(m, sc[i]);
+  }
+  // chunk max over the workgroup
+#pragma unroll
+  for (int o = TPR; o < 64; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kAttnThreads / 64; ++w) m = __builtin_fmaxf(m, wmax[w]);
+
+  // ---- weights, their sum (each token counted by its lane 0 of the row), code-space output
+  float l = 0.0f;
+  float o16[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o16[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const float p = __builtin_amdgcn_exp2f(sc[i] - m);  // 0 for rows past the end
+    if (lc == 0) l += p;
+    const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o16[j] = __builtin_fmaf(p, (float)((w[j >> 2] >> (8 * (j & 3))) & 0xFFu), o16[j]);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+  if (lane == 0) wsum[wave] = l;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) red[rr][lc * 16 + j] = o16[j];
+  __syncthreads();
+  float* out = ws + (((size_t)qi * heads + h) * gridDim.x + chunk) * (D + 2);
+  if (tid < D) {
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < ROWS; ++r) acc += red[r][tid];
+    out[2 + tid] = acc;
+  }
+  if (tid == 0) {
+    float lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnThreads / 64; ++w) lt += wsum[w];
+    out[0] = m;
+    out[1] = lt;
+  }
+}
+
+// Combine: 256 threads per (head, query).  The chunk weights 2^(m_i - M) are computed once
+// (threads over chunks) into LDS, then thread (d, part) sums the rescaled code-space partials of
+// channel d over every (256 / D)-th chunk, several loads in flight, and the parts meet in LDS.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineChunksLds = 4096;  // chunk weights kept in LDS (1M tokens)
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void kv_attn_combine_kernel(
+    const float* __restrict__ ws, const float* __restrict__ vs, const uint8_t* __restrict__ vz,
+    int heads, int nchunks, uint16_t* __restrict__ out) {
+  constexpr int PARTS = kCombineThreads / D;
+  __shared__ float fw[kCombineChunksLds];
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float osum[PARTS][D];
+  const int h = blockIdx.x, qi = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* part = ws + ((size_t)qi * heads + h) * nchunks * (D + 2);
+  // M = max_i m_i
+  float M = -__builtin_inff();
+  for (int i = tid; i < nchunks; i += kCombineThreads) M = __builtin_fmaxf(M, part[(size_t)i * (D + 2)]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = __builtin_fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) M = __builtin_fmaxf(M, red[w]);
+  __syncthreads();
+  // weights f_i and L = sum_i l_i f_i
+  float L = 0.0f;
+  for (int i = tid; i < nchunks; i += kCombineThreads) {
+    const float f = __builtin_amdgcn_exp2f(part[(size_t)i * (D + 2)] - M);
+    fw[i] = f;
+    L = __builtin_fmaf(part[(size_t)i * (D + 2) + 1], f, L);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+  if (lane == 0) red[wave] = L;
+  __syncthreads();
+  L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) L += red[w];
+  // O_d = sum_i O_id f_i, chunks split over the parts
+  const int d = tid % D, pt = tid / D;
+  float O = 0.0f;
+  int i = pt;
+  for (; i + 3 * PARTS < nchunks; i += 4 * PARTS) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = part[(size_t)(i + u * PARTS) * (D + 2) + 2 + d];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) O = __builtin_fmaf(v[u], fw[i + u * PARTS], O);
+  }
+  for (; i < nchunks; i += PARTS) O = __builtin_fmaf(part[(size_t)i * (D + 2) + 2 + d], fw[i], O);
+  osum[pt][d] = O;
+  __syncthreads();
+  if (tid < D) {
+    O = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) O += osum[p][tid];
+    const int c = h * D + tid;
+    out[((size_t)qi * heads + h) * D + tid] = float_to_bf16_bits(vs[c] * (O - (float)vz[c] * L) / L);
+  }
+}
+
+size_t kv_attn_workspace_bytes(int nq, int tokens, int heads, int dim) {
+  if (nq <= 0 || tokens <= 0 || heads <= 0 || dim <= 0) return 0;
+  return (size_t)nq * heads * attn_chunks(tokens) * (dim + 2) * sizeof(float);
+}
+
+hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kq, const float* ks,
+                               const uint8_t* kz, const uint8_t* vq, const float* vs,
+                               const uint8_t* vz, int nq, int tokens, int heads, int dim,
+                               float sm_scale, uint16_t* out, void* workspace,
+                               hipStream_t stream) {
+  const int nchunks = attn_chunks(tokens);
+  float* ws = reinterpret_cast<float*>(workspace);
+  const float qscale = sm_scale * 1.4426950408889634f;  // log2(e): the weights use exp2
+  const dim3 grid(nchunks, heads, nq);
+  if (dim == 128) {
+    hipLaunchKernelGGL(kv_attn_partial_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, kq,
+                       ks, kz, vq, tokens, heads, qscale, ws);
+  } else if (dim == 64) {
+    hipLaunchKernelGGL(kv_attn_partial_kernel<64>, grid, dim3(kAttnThreads), 0, stream, q, kq,
+                       ks, kz, vq, tokens, heads, qscale, ws);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dim == 128)
+    hipLaunchKernelGGL(kv_attn_combine_kernel<128>, dim3(heads, nq), dim3(kCombineThreads), 0,
+                       stream, ws, vs, vz, heads, nchunks, out);
+  else
+    hipLaunchKernelGGL(kv_attn_combine_kernel<64>, dim3(heads, nq), dim3(kCombineThreads), 0,
+                       stream, ws, vs, vz, heads, nchunks, out);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -44,4 +44,13 @@ hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t*
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,
                              int tokens, int channels, uint16_t* x_out, hipStream_t stream);
 
+// decode attention over the INT8 cache (codes, per-channel scale / zero of K and V)
+size_t kv_attn_workspace_bytes(int nq, int tokens, int heads, int dim);
+
+hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kq, const float* ks,
+                               const uint8_t* kz, const uint8_t* vq, const float* vs,
+                               const uint8_t* vz, int nq, int tokens, int heads, int dim,
+                               float sm_scale, uint16_t* out, void* workspace,
+                               hipStream_t stream);
+
 }  // namespace svdq

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 3
+#define SVDQ_ABI_VERSION 4
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -212,6 +212,29 @@ int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float
  */
 int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
                     int channels, uint16_t* x_out, void* stream);
+
+/*
+ * kv_int8_attention — decode attention that reads the INT8 cache written by kv_int8_quant
+ * (the consumer that turns the cache's memory saving into a bandwidth saving; VARC "INT8 KV
+ * cache quantization").  For every query i and head h, over all tokens t:
+ *     K'[t, c] = (k_codes[t, c] - k_zero[c]) k_scale[c],  V' likewise,  c = h dim + d,
+ *     out[i, h, :] = softmax_t(sm_scale q[i, h, :] . K'[t, h, :]) V'[t, h, :]
+ * evaluated in fp32 (scores, weights and the code-space sums) and rounded to bf16.
+ *   q          bf16 [nq, heads, dim]                                   16B
+ *   k_codes, v_codes   uint8 [tokens, heads dim] as written by kv_int8_quant   16B
+ *   k_scale, k_zero    fp32 / uint8 [heads dim] (16B); v_scale, v_zero likewise
+ *   out        bf16 [nq, heads, dim]
+ *   workspace  device scratch of kv_int8_attention_workspace_bytes(nq, tokens, heads, dim)
+ *              bytes (16B): one partial (max, sum, dim code-space sums) per query, head and
+ *              256-token chunk; no initialization needed, fully rewritten by every call; calls
+ *              that share one workspace must not overlap in time.
+ *   nq >= 1, 1 <= tokens <= 2^20, heads >= 1, dim 64 or 128, sm_scale finite.
+ */
+size_t kv_int8_attention_workspace_bytes(int nq, int tokens, int heads, int dim);
+int kv_int8_attention(const uint16_t* q, const uint8_t* k_codes, const float* k_scale,
+                      const uint8_t* k_zero, const uint8_t* v_codes, const float* v_scale,
+                      const uint8_t* v_zero, int nq, int tokens, int heads, int dim,
+                      float sm_scale, uint16_t* out, void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 3
+    assert lib.svdq_abi_version() == 4
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -141,6 +141,21 @@ def test_kv_validation(lib):
     d = lib.kv_int8_dequant
     assert d(FAKE, FAKE, FAKE, 16, 0, FAKE, None) == binding.SVDQ_EINVAL
     assert d(FAKE, FAKE, FAKE, 16, 16, ODD, None) == binding.SVDQ_EALIGN
+
+
+def test_kv_attention_validation(lib):
+    assert lib.kv_int8_attention_workspace_bytes(1, 10240, 32, 128) == 32 * 40 * 130 * 4
+    assert lib.kv_int8_attention_workspace_bytes(2, 257, 4, 64) == 2 * 4 * 2 * 66 * 4
+    assert lib.kv_int8_attention_workspace_bytes(0, 16, 4, 64) == 0
+    a = lib.kv_int8_attention
+    p7 = [FAKE] * 7
+    assert a(*p7, 1, 16, 4, 96, 0.1, FAKE, FAKE, None) == binding.SVDQ_ESHAPE     # dim
+    assert a(*p7, 0, 16, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EINVAL     # nq
+    assert a(*p7, 1, 0, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EINVAL      # no tokens
+    assert a(*p7, 1, 16, 4, 64, 0.1, FAKE, None, None) == binding.SVDQ_EINVAL     # workspace
+    assert a(ODD, *p7[1:], 1, 16, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    assert a(*p7, 1, 16, 4, 64, float("nan"), FAKE, FAKE, None) == binding.SVDQ_EINVAL
+    assert b"sm_scale" in lib.svdq_last_error()
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
