@@ -6,15 +6,14 @@
 // partial P[g] = qx[:, g] . qw[g, :] is exact, and
 //     Y = sum_g diag(s_x[g]) P[g] diag(s_w[g]) + bf16(T) L2 + bias.
 //
-// gfx950 mapping (one workgroup = 8 waves = a 256 x 256 tile of Y; wave (wm, wn) owns the
-// 128 x 64 sub-tile made of 8 x 4 tiles of 16 x 16):
-//  * Staging.  Per 64-group the tile needs 256 packed rows of xq and 256 packed columns of wq
-//    (32 bytes each).  Every thread loads 16 packed bytes of each with one 16-byte load,
-//    unpacks them to int8 holding 16 * code (see unpack16_x16) and writes them to LDS, so each
+// gfx950 mapping (one workgroup = 4 waves = a 128 x 128 tile of Y; wave (wm, wn) owns the
+// 64 x 64 sub-tile made of 4 x 4 tiles of 16 x 16):
+//  * Staging.  Per 64-group the tile needs 128 packed rows of xq and 128 packed columns of wq
+//    (32 bytes each).  Threads load 16 packed bytes per segment into registers one group ahead,
+//    unpack them to int8 holding 16 * code (see unpack16_x16) and write them to LDS, so each
 //    code is unpacked once per workgroup rather than once per wave.  Rows are padded to 80
 //    bytes: the 16 lanes that read one MFMA fragment hit 16 disjoint bank quads.  Two LDS
-//    buffers alternate; the next group's global loads are in flight while the current group
-//    is computed, and one barrier per group separates the phases.
+//    buffers alternate, and one barrier per group separates the phases.
 //  * Integer products.  v_mfma_i32_16x16x64_i8 covers exactly one group, so each result is
 //    256 * P[g] for one 16 x 16 tile; operands are single 16-byte LDS reads.
 //  * Scale products.  s_x[m] * s_w[n] is an outer product, which v_mfma_f32_16x16x32_f16
