@@ -99,3 +99,27 @@ def test_end_to_end_from_the_gpu_quantizer(gpu_lib):
     full = np.stack([np.exp(s - s.max()) / np.exp(s - s.max()).sum() @ V[:, h]
                      for h in range(heads) for s in [K[:, h] @ qd[h] / math.sqrt(dim)]])
     assert max_abs_rel(out.float().cpu().numpy()[0].astype(np.float64), full) <= 0.05
+
+
+def test_workspace_needs_no_initialization_and_is_reusable(gpu_lib):
+    # every call rewrites the partials it reads: garbage in a fresh workspace and partials left
+    # by earlier calls (also of another shape) never leak into a result
+    tokens, heads, dim = 900, 4, 128
+    cache = _cache(tokens, heads, dim, seed=3)
+    small = _cache(300, heads, dim, seed=4)
+    rng = np.random.default_rng(11)
+    qs = [bf16_to_bits(round_bf16(rng.standard_normal((2, heads, dim)))) for _ in range(3)]
+    ws = torch.full((B.kv_int8_attention_workspace_bytes(2, tokens, heads, dim),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    outs = []
+    for i, qb in enumerate(qs + qs):
+        c = cache if i % 2 == 0 else small
+        o = torch.empty(2, heads, dim, dtype=torch.bfloat16, device="cuda")
+        (kq, ks, kz), (vq, vs, vz) = c["K"], c["V"]
+        B.kv_int8_attention(dev_bf16(qb), dev(kq), dev(ks), dev(kz), dev(vq), dev(vs), dev(vz),
+                            1.0 / math.sqrt(dim), o, ws)   # no synchronization between calls
+        outs.append((qb, c, o))
+    torch.cuda.synchronize()
+    for qb, c, o in outs:
+        ref = oka.attention(qb, *c["K"], *c["V"], heads, dim, 1.0 / math.sqrt(dim))
+        assert max_abs_rel(o.float().cpu().numpy().astype(np.float64), ref) <= TOL
