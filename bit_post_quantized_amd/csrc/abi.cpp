@@ -136,6 +136,7 @@ static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K)
   if ((long long)M * N > kMaxElems || (long long)M * K > kMaxElems || (long long)N * K > kMaxElems)
     return fail(SVDQ_ESHAPE, "problem too large");
   if ((M + 127) / 128 > 65535) return fail(SVDQ_ESHAPE, "M too large for one launch");
+  if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535 (got K = %d)", K);
   if (!xq || !wq) return fail(SVDQ_EINVAL, "NULL pointer");
   if (!aligned16(xq) || !aligned16(wq)) return fail(SVDQ_EALIGN, "xq and wq must be 16-byte aligned");
   return SVDQ_OK;

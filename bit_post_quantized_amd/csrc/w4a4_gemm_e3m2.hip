@@ -65,6 +65,43 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+// gfx9 buffer resource over [base, base + bytes): raw (stride 0), dword data format.  A load at
+// an offset past `bytes` returns zero and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// The four resources of one stage (first group g0), all uniform (scalar registers): the codes
+// of the workgroup's row and column blocks from group g0 to the end of the tensor (counted in
+// 32-bit units: blocks left = (row blocks from the tile on) * G - g0 <= 2^29 for M * K <= 2^40,
+// capped at 2^31 - 1 bytes, beyond every offset a stage uses), and the TM (TN) scales of the
+// wave's group g0 + s_gq from the tile's first row -- or nothing when that group does not exist
+// (the second group of an odd G's last stage).
+struct StageRsrc {
+  __amdgpu_buffer_rsrc_t a, b, sx, sw;
+};
+template <bool PARTIALS>
+__device__ __forceinline__ StageRsrc stage_rsrc(const uint8_t* xq, const uint8_t* wq,
+                                                const uint16_t* x_scales, const uint16_t* w_scales,
+                                                int M, int N, int G, int mt, int nt, int m_tile,
+                                                int n_tile, int g0, int s_gq, int TM, int TN) {
+  constexpr int kFrag = kE3m2Block, kCap = 0x7FFFFFFF / kFrag;
+  StageRsrc R;
+  const int ab = ((M + 31) / 32 - mt) * G - g0, bb = ((N + 31) / 32 - nt) * G - g0;
+  R.a = buffer_rsrc(xq + ((size_t)mt * G + g0) * kFrag, ab >= kCap ? 0x7FFFFFFF : ab * kFrag);
+  R.b = buffer_rsrc(wq + ((size_t)nt * G + g0) * kFrag, bb >= kCap ? 0x7FFFFFFF : bb * kFrag);
+  if constexpr (!PARTIALS) {
+    const int g = g0 + s_gq;
+    const bool live = g < G;
+    R.sx = buffer_rsrc(x_scales + (size_t)min(g, G - 1) * M + m_tile, live ? 2 * TM : 0);
+    R.sw = buffer_rsrc(w_scales + (size_t)min(g, G - 1) * N + n_tile, live ? 2 * TN : 0);
+  } else {
+    R.sx = R.a;
+    R.sw = R.b;
+  }
+  return R;
+}
+
 // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding: vmcnt in bits 3..0
 // and 15..14, expcnt 6..4, lgkmcnt 11..8)
 #define SVDQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -92,55 +129,44 @@ void w4a4_gemm_e3m2_kernel(
   //      KS consecutive blocks per 32-row tile into LDS ([tile][group][64 slots][24 B]).  Load j
   //      of thread t moves 16-byte chunk c = j * 256 + t of the stage (each load instruction of
   //      a wave fills 1 KB of consecutive LDS, lane l at +16 l): byte 16 (c % 96) of the block
-  //      (tile (c / 96) / KS, group (c / 96) % KS) -- a fixed per-lane pointer plus the stage's
-  //      uniform group offset.  Tiles past the last row block re-read that block (unused rows).
+  //      (tile (c / 96) / KS, group (c / 96) % KS).  The loads are buffer loads: a uniform
+  //      base (the workgroup's first row block, advanced to the stage's first group) in a buffer
+  //      resource, plus a fixed 32-bit per-lane offset, so they cost no VALU work.  Each
+  //      resource ends where its tensor ends, so the loads of the missing second group of an
+  //      odd G's last stage read the next row block or nothing (out of range), and are never
+  //      used.  Tiles past the last row block re-read that block (unused rows).
   const int G = K / kGroup;
   const int mblk = (M + 31) / 32, nblk = (N + 31) / 32;
-  const uint8_t* a_ptr[kLoadsA];
-  const uint8_t* b_ptr[kLoadsB];
-  int a_g[kLoadsA];
+  const int mt = m_tile / 32, nt = n_tile / 32;
+  uint32_t a_off[kLoadsA], b_off[kLoadsB];  // < 4 G kFrag < 2^31 (K / 64 <= 65535)
 #pragma unroll
   for (int j = 0; j < kLoadsA; ++j) {
     const int c = j * THREADS + tid, blk = c / 96;
     const int tile = blk / KS;
-    a_g[j] = blk % KS;
-    const size_t within = (size_t)a_g[j] * kFrag + (c % 96) * 16;
-    a_ptr[j] = xq + (size_t)min(m_tile / 32 + tile, mblk - 1) * G * kFrag + within;
-    b_ptr[j] = wq + (size_t)min(n_tile / 32 + tile, nblk - 1) * G * kFrag + within;
+    const size_t within = (size_t)(blk % KS) * kFrag + (c % 96) * 16;
+    a_off[j] = (uint32_t)((size_t)(min(mt + tile, mblk - 1) - mt) * G * kFrag + within);
+    b_off[j] = (uint32_t)((size_t)(min(nt + tile, nblk - 1) - nt) * G * kFrag + within);
   }
   // scales: thread t loads s_x of (group t / TM, row t % TM) and s_w of (group t / TN,
   // column t % TN) as 2-byte direct loads, which land zero-extended in dword t of the area;
   // the group of a scale load is uniform over the wave
   const int s_gq = wave >> 1;
-  const uint16_t* sx_ptr = PARTIALS ? nullptr : x_scales + (size_t)s_gq * M + min(m_tile + tid % TM, M - 1);
-  const uint16_t* sw_ptr = PARTIALS ? nullptr : w_scales + (size_t)s_gq * N + min(n_tile + tid % TN, N - 1);
+  const uint32_t sx_lane = 2u * (uint32_t)(min(m_tile + tid % TM, M - 1) - m_tile);
+  const uint32_t sw_lane = 2u * (uint32_t)(min(n_tile + tid % TN, N - 1) - n_tile);
 
   auto issue_stage = [&](int s) {
     uint8_t* st = lds + (s % NB) * kStage;
     const int g0 = s * KS;
-    if (g0 + KS <= G) {  // every stage but the last one of an odd G
-      if constexpr (!PARTIALS) {
-        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g0 * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
-        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g0 * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
-      }
-      const size_t go = (size_t)g0 * kFrag;
+    const StageRsrc R = stage_rsrc<PARTIALS>(xq, wq, x_scales, w_scales, M, N, G, mt, nt, m_tile,
+                                             n_tile, g0, s_gq, TM, TN);
+    if constexpr (!PARTIALS) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(R.sx, SVDQ_LDS(st + wave * 256), 2, sx_lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(R.sw, SVDQ_LDS(st + kScA + wave * 256), 2, sw_lane, 0, 0, 0);
+    }
 #pragma unroll
-      for (int j = 0; j < kLoadsA; ++j) {
-        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
-      }
-    } else {  // groups past the end re-read group G - 1 (loaded, never used)
-      if constexpr (!PARTIALS) {
-        const int g = min(g0 + s_gq, G - 1) - s_gq;
-        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
-        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < kLoadsA; ++j) {
-        const size_t go = (size_t)(min(g0 + a_g[j], G - 1) - a_g[j]) * kFrag;
-        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
-      }
+    for (int j = 0; j < kLoadsA; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(R.a, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, a_off[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(R.b, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, b_off[j], 0, 0, 0);
     }
   };
 
@@ -149,23 +175,19 @@ void w4a4_gemm_e3m2_kernel(
   // one burst, which would hold the wave at the memory pipeline ahead of its MFMAs.
   // Order: A0, B0, A1, B1, A2, B2, then the s_x and s_w scales.
   static_assert(kLoadsA == kLoadsB && 2 * kLoadsA + 2 <= KS * 4, "one load per tile");
-  auto issue_load = [&](int s, int idx) {
+  auto issue_load = [&](int s, const StageRsrc& R, int idx) {
     uint8_t* st = lds + (s % NB) * kStage;
-    const int g0 = s * KS;
-    const bool full = g0 + KS <= G;  // every stage but the last one of an odd G
     if (idx < 2 * kLoadsA) {
       const int j = idx >> 1;
-      const size_t go = (size_t)(full ? g0 : min(g0 + a_g[j], G - 1) - a_g[j]) * kFrag;
       if (idx & 1)
-        __builtin_amdgcn_global_load_lds(b_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(R.b, SVDQ_LDS(st + kScA + kScB + kOpA + j * 4096 + wave * 1024), 16, b_off[j], 0, 0, 0);
       else
-        __builtin_amdgcn_global_load_lds(a_ptr[j] + go, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(R.a, SVDQ_LDS(st + kScA + kScB + j * 4096 + wave * 1024), 16, a_off[j], 0, 0, 0);
     } else if constexpr (!PARTIALS) {
-      const int g = full ? g0 : min(g0 + s_gq, G - 1) - s_gq;
       if (idx == 2 * kLoadsA)
-        __builtin_amdgcn_global_load_lds(sx_ptr + (size_t)g * M, SVDQ_LDS(st + wave * 256), 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(R.sx, SVDQ_LDS(st + wave * 256), 2, sx_lane, 0, 0, 0);
       else
-        __builtin_amdgcn_global_load_lds(sw_ptr + (size_t)g * N, SVDQ_LDS(st + kScA + wave * 256), 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(R.sw, SVDQ_LDS(st + kScA + wave * 256), 2, sw_lane, 0, 0, 0);
     }
   };
 
@@ -311,6 +333,10 @@ void w4a4_gemm_e3m2_kernel(
     // last two)
     auto stage = [&](int s, auto issue_tag) {
       constexpr bool ISSUE = decltype(issue_tag)::value;
+      StageRsrc R2{};
+      if constexpr (ISSUE)
+        R2 = stage_rsrc<false>(xq, wq, x_scales, w_scales, M, N, G, mt, nt, m_tile, n_tile,
+                               (s + 2) * KS, s_gq, TM, TN);
       wait_stage(s);
       if (s == max(S - 2, 0)) issue_prefetch();
       const uint8_t* st = lds + (s % NB) * kStage;
@@ -329,7 +355,7 @@ void w4a4_gemm_e3m2_kernel(
         for (int t = 0; t < 4; ++t) {
           const int i = t >> 1, j = t & 1, li = gg * 4 + t;
           const v16f pn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(C.A[i], C.B[j], zero16, 3, 3, 0, 127, 0, 127);
-          if (ISSUE && li < kLoads) issue_load(s + 2, li);
+          if (ISSUE && li < kLoads) issue_load(s + 2, R2, li);
           // (also in a last stage without a second group: its LDS holds a valid duplicate)
           if (t == 0 && gg + 1 < KS) read_frag(st, gg + 1, F[gg + 1]);
           // the pending tile: (1, 1) of the previous group at t == 0, else tile t - 1

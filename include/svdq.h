@@ -102,7 +102,8 @@ int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t
  *   bias        bf16 [N] or NULL
  *   Y           [M, N], bf16 (out_dtype = SVDQ_OUT_BF16, round to nearest even) or fp32
  *               (SVDQ_OUT_FP32)                           16B
- *   M >= 0, N >= 1, K % 64 == 0, K >= 64, 0 <= r <= 128, r % 16 == 0.
+ *   M >= 0, N >= 1, K % 64 == 0, 64 <= K <= 64 * 65535 (the packer's limit), 0 <= r <= 128,
+ *   r % 16 == 0.  The same limits hold for every GEMM entry point below.
  */
 int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
                    const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,

@@ -74,6 +74,7 @@ def test_gemm_validation(lib):
     assert g(*args, 8, 0, 128, 0, FAKE, 0, None) == binding.SVDQ_EINVAL
     assert g(*args, 8, 8, 128, 0, FAKE, 7, None) == binding.SVDQ_EINVAL  # bad out_dtype
     assert g(*args, 8, 8, 128, 24, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert g(*args, 8, 8, 64 * 65536, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE  # K / 64 > 65535
     assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 8, 8, 128, 16, FAKE, 0, None) == binding.SVDQ_EINVAL
     assert g(*args, 8, 8, 128, 0, ODD, 0, None) == binding.SVDQ_EALIGN
     assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK
