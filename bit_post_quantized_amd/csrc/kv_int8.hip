@@ -10,8 +10,8 @@
 //
 // Two schedules compute the same codes:
 //  * the fused single pass (kv_quant_fused_kernel, below) reads x from HBM once and keeps it in
-//    registers while the blocks that share a 64-channel slab agree on its range through the
-//    workspace.  It runs when channels are a multiple of 64, a quarter of the tokens fits in
+//    registers while the blocks that share a 128-channel slab agree on its range through the
+//    workspace.  It runs when channels are a multiple of 128, an eighth of the tokens fits in
 //    40 rows per thread, and the device holds the whole grid at once.
 //  * otherwise three launches, no atomics and no grid barrier:
 //   1. kv_range_kernel: a block owns 512 channels x 64 tokens (the blocks of one token chunk
@@ -292,21 +292,24 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restri
 
 // ---------------------------------------------------------------- fused single pass
 // x is read from HBM once: a block keeps its share of x in registers while the per-channel
-// range is agreed, then codes it from registers.  A slab of 64 channels (one 128-byte line of a
-// bf16 row) is split over kFusedParts blocks by tokens; each block folds min / max over its
+// range is agreed, then codes it from registers.  A slab of 128 channels (256 bytes of a bf16
+// row, one whole 128-byte line of its codes) is split over kFusedParts blocks by tokens (a
+// 64-channel slab writes half lines, which two XCDs then write back separately, and loads
+// 128-byte strips; both measured slower); each block folds min / max over its
 // tokens, publishes the partial range in the workspace with the call's epoch as a tag, waits
 // for the other parts' tags, folds the parts, and quantizes.  The parts of a slab are mapped
 // to blocks that the dispatcher places on one XCD (block b runs on XCD b % 8), so the exchange
 // mostly stays in one L2.  The wait is bounded: a block that times out (e.g. when not every
 // part of its slab is resident) computes the slab's range from x itself, so the result never
 // depends on the exchange and the kernel always finishes.
-constexpr int kFusedCh = 64;
-constexpr int kFusedParts = 4;
+constexpr int kFusedCh = 128;
+constexpr int kFusedParts = 8;
 constexpr int kFusedThreads = 512;
-constexpr int kFusedRowThreads = kFusedCh / kKvLanesC;                // 8 threads share a row
-constexpr int kFusedRowsPerPass = kFusedThreads / kFusedRowThreads;   // 64 rows per pass
+constexpr int kFusedRowThreads = kFusedCh / kKvLanesC;                // 16 threads share a row
+constexpr int kFusedRowsPerPass = kFusedThreads / kFusedRowThreads;   // 32 rows per pass
 constexpr int kFusedMaxRows = 40;                                     // rows per thread
-constexpr int kFusedSegs = kFusedThreads / kFusedCh;                  // 8 fold segments
+constexpr int kFusedSegs = kFusedThreads / kFusedCh;                  // 4 fold segments of 8 rows
+static_assert(kFusedSegs * 8 == kFusedRowsPerPass, "block fold: segments of 8 rows");
 constexpr int kFusedInFlight = 8;                                     // row loads in flight
 
 __device__ __forceinline__ void fused_slab_part(int b, int nslabs, int& slab, int& part) {
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
       hi[i] = __builtin_fmaxf(hi[i], f[i]);
     }
   }
-  // block fold: 64 row-threads per channel -> 8 segments of 8 rows in LDS -> 1
+  // block fold: kFusedRowsPerPass row-threads per channel -> segments of 8 rows in LDS -> 1
   auto block_fold = [&](float* out_lo, float* out_hi) {
     __shared__ float stage[2][kFusedRowsPerPass][kFusedCh + 1];
 #pragma unroll
