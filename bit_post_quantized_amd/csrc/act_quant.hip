@@ -12,7 +12,7 @@
 // [16 q, 16 q + 16) of quarter q = l / 16: two 16-byte loads, so every load instruction reads
 // 16 rows x 64 contiguous bytes.  The loads of kActBatch groups are issued before any of them is
 // used; inv_lambda sits in LDS.  The group max is folded over the four quarter lanes of a row
-// with two lane shuffles; every lane then codes its 16 values (exact quotient, no division per
+// with two VALU lane swaps; every lane then codes its 16 values (exact quotient, no division per
 // element) as biased bytes c + 2^(b-1) and writes them in one of three containers: 8 bytes of
 // nibbles, 12 bytes of BF6 (E3M2) patterns into the tiled container (its row block, group,
 // slot row % 32 + 32 (q / 2), byte 12 (q % 2)), or 16 bytes of int8.  The quarter-0 lanes write
@@ -29,9 +29,24 @@
 namespace svdq {
 
 constexpr int kActRows = 16;    // tokens per workgroup
-constexpr int kActBatch = 6;    // groups per wave whose code loads are in flight together
-constexpr int kActMaxWaves = 8;
+constexpr int kActBatch = 3;    // groups per wave whose code loads are in flight together
+// up to 16 waves (4 per SIMD at <= 128 VGPRs) share a workgroup's groups: at K = 3072 each
+// takes one batch of 3; 8 waves of 6 groups hid less latency (27.3 against 25.6 us at
+// 4608 x 3072)
+constexpr int kActMaxWaves = 16;
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
+
+// max over the four quarter lanes l, l ^ 16, l ^ 32, l ^ 48 of a row.  gfx950's permlane
+// swaps exchange 16-lane rows (0 <-> 1, 2 <-> 3) and 32-lane halves between two registers in
+// the VALU; given the same value twice, the two results of a swap hold a lane's own value and
+// its partner's in some order, so their max is the pair's max (no LDS round trip, as a
+// ds_bpermute shuffle would take).
+__device__ __forceinline__ float max_row_quarters(float a) {
+  const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __builtin_fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
 
 // CODES: kCodesNibbles, kCodesBf6 (INT4 codes) or kCodesInt8 (8-bit codes of the W4A8 variant)
 template <int NTR, int CODES, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
@@ -133,8 +148,7 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+      amax = max_row_quarters(amax);
       constexpr bool I8 = CODES == kCodesInt8;
       const uint16_t sb = I8 ? float_to_half_bits(amax / 127.0f) : int4_scale_bits(amax);
       const float s = half_bits_to_float(sb);
