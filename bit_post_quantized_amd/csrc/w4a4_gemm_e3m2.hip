@@ -18,9 +18,11 @@
 //    l of a (row block, group) block of the tiled container.  The 32 x 32 result: lane l holds
 //    column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..15.
 //  * Staging.  KS = 2 groups per stage, NB = 3 stages resident in LDS, two of them in flight:
-//    codes and scales go from global memory straight into LDS (global_load_lds, 16-byte and
-//    2-byte), so no registers or VALU work are spent on staging and the loads of stage s + 2
-//    are issued while stage s is computed.  The tiled container's blocks are copied as they
+//    codes and scales go from global memory straight into LDS (buffer loads with the LDS
+//    destination, 16-byte and 2-byte, from a scalar buffer resource per stage), so no
+//    registers or VALU work are spent on staging and the loads of stage s + 2 are issued
+//    while stage s is computed.  (The epilogue's T, L2 and bias, loaded once per tile, use
+//    global_load_lds.)  The tiled container's blocks are copied as they
 //    are, so an MFMA operand is three ds_read_b64 per lane from its 24-byte slot.
 //  * Scale products.  s_x[m] * s_w[n] for a 32 x 32 tile is an outer product that
 //    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) from one fp16 per
