@@ -41,6 +41,7 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
 FP6_PEAK_TOPS = 10100.0      # MI355X dense FP6 MFMA, 10.1 PFLOP/s (the GEMM's matrix dtype)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, 8 TB/s
 M, K, N, RANK = 4608, 3072, 12288, 32
+LORA_RANK = 16   # adapter rank of the LoRA line (reported beside the product path)
 KV_T, KV_H, KV_D = 10240, 32, 128
 ROTATE = 3
 
@@ -244,6 +245,19 @@ def main():
         "gemm": time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
                                                 stream)),
     }
+    # LoRA: a seeded rank-16 adapter joined to the 16-bit branch (rank 32 + 16 = 48), FP6 route,
+    # the residual's codes and scales shared with the base layer
+    gl = torch.Generator().manual_seed(7)
+    pwl = layer.attach_lora(pw, torch.randn(K, LORA_RANK, generator=gl, dtype=torch.float64) * 0.02,
+                            torch.randn(LORA_RANK, N, generator=gl, dtype=torch.float64) * 0.02)
+    al = layer.alloc_act(M, K, pwl.rank, dev, e3m2=True)
+    lora_ms = {
+        "act": time10(lambda: B.svdq_quantize_act_e3m2(X[0], pwl.inv_lambda, pwl.L1t, pwl.rank,
+                                                       al.xq, al.x_scales, al.T, stream)),
+        "gemm": time10(lambda: B.svdq_w4a4_gemm_e3m2(al.xq, al.x_scales, al.T, pwl.wq,
+                                                     pwl.w_scales, pwl.L2t, None, pwl.rank, Y[0],
+                                                     stream)),
+    }
     # decode attention over the INT8 cache of batch 0 (one query per head): reads the codes
     q_att = torch.randn(1, KV_H, KV_D, device=dev).to(torch.bfloat16)
     o_att = torch.empty(1, KV_H, KV_D, dtype=torch.bfloat16, device=dev)
@@ -298,6 +312,11 @@ def main():
         "w4a8_route": {"gemm_ms": round(w4a8_ms["gemm"], 5), "act_ms": round(w4a8_ms["act"], 5),
                        "gemm_TOPS": round(gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12, 2),
                        "pct_int8_peak": round(100.0 * gemm_ops / (w4a8_ms["gemm"] * 1e-3) / 1e12
+                                              / INT8_PEAK_TOPS, 2)},
+        "lora_route": {"rank": RANK + LORA_RANK, "adapter_rank": LORA_RANK,
+                       "gemm_ms": round(lora_ms["gemm"], 5), "act_ms": round(lora_ms["act"], 5),
+                       "gemm_TOPS": round(gemm_ops / (lora_ms["gemm"] * 1e-3) / 1e12, 2),
+                       "pct_int8_peak": round(100.0 * gemm_ops / (lora_ms["gemm"] * 1e-3) / 1e12
                                               / INT8_PEAK_TOPS, 2)},
         "kv_attention": {"ms": round(attn_ms, 5), "queries": 1,
                          "GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
