@@ -148,6 +148,20 @@ def test_partials_e3m2_bitexact(gpu_lib, name):
     np.testing.assert_array_equal(P.cpu().numpy(), osq.int_partials(ref["codes"][:M], case[2]["codes"][:N]))
 
 
+@pytest.mark.parametrize("K", [64, 192, 320])  # G = 1, 3, 5: the last stage holds one group
+def test_partials_e3m2_odd_groups_bitexact(gpu_lib, K):
+    # the missing second group of the last stage is loaded from the next row block, or out of
+    # range for the tensor's last row block, and never used
+    case = linear_case(2, 70, K, 100)
+    xq6, xs, T = _gpu_act6(case)
+    wq6, ws = _gpu_pack6(case)
+    P = torch.empty(K // 64, 70, 100, dtype=torch.int32, device="cuda")
+    B.svdq_w4a4_partials_e3m2(xq6, wq6, 70, 100, K, P)
+    torch.cuda.synchronize()
+    ref = oracle_act(case)
+    np.testing.assert_array_equal(P.cpu().numpy(), osq.int_partials(ref["codes"], case[2]["codes"]))
+
+
 def test_e3m2_and_nibble_routes_agree(gpu_lib):
     """Same codes in both containers, and the same Y up to fp32 summation order."""
     case = _case("c3s", bias=True)
