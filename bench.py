@@ -211,7 +211,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    samples = {n: np.array([a.elapsed_time(b) for a, b in ev[n]]) * 1e3 for n in names}  # us
+    ms = {n: float(samples[n].mean()) * 1e-3 for n in names}
+    stats_us = {n: {"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+                    "p90": round(float(np.percentile(v, 90)), 2), "calls": int(v.size)}
+                for n, v in samples.items()}
 
     # ---- the INT8-unit route on the same batch, outside the timed region
     B.svdq_pack_weights(pw.R32, wq4, ws4)
@@ -305,6 +309,7 @@ def main():
         "act_quant_GBps": round(gbps["act"], 1),
         "linear_TOPS": round(gemm_ops / ((ms["act"] + ms["gemm"]) * 1e-3) / 1e12, 2),
         "kernel_ms": {n: round(v, 5) for n, v in ms.items()},
+        "kernel_us_stats": stats_us,
         "int8_route": {"gemm_ms": round(int8_ms["gemm"], 5), "act_ms": round(int8_ms["act"], 5),
                        "gemm_TOPS": round(gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12, 2),
                        "pct_int8_peak": round(100.0 * gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12
