@@ -91,6 +91,35 @@ def algorithmic_bytes():
     return dict(act=act, kv_quant=kvq, kv_dequant=kvd, gemm=gemm)
 
 
+def clock_reader():
+    """A function returning (graphics MHz, memory MHz) of the first GPU now, or None when the
+    ROCm SMI library is not usable here (the clocks are then reported as null)."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+
+        def read():
+            return (amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"],
+                    amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
+        read()
+        return read
+    except Exception:  # no SMI library, no permission, no device: clocks are context only
+        return None
+
+
+def clock_summary(samples):
+    if not samples:
+        return None
+    g = [a for a, _ in samples if isinstance(a, (int, float))]
+    m = [b for _, b in samples if isinstance(b, (int, float))]
+    if not g or not m:
+        return None
+    return {"sclk_mhz": {"mean": round(float(np.mean(g))), "min": min(g), "max": max(g)},
+            "mclk_mhz": {"mean": round(float(np.mean(m))), "min": min(m), "max": max(m)},
+            "samples": len(samples)}
+
+
 def cpu_baseline(rows: int):
     """The oracle (as it stands) on a bounded sample: `rows` tokens of the same workload."""
     from oracle import svdquant as osq
@@ -203,11 +232,21 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    read_clock = clock_reader()
     ev = {n: [] for n in names}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, ev)
+    # clocks while the queued steps run (a few ms of host time, well inside the GPU's backlog)
+    clk = []
+    if read_clock is not None:
+        for _ in range(8):
+            try:
+                clk.append(read_clock())
+            except Exception:
+                break
+            time.sleep(0.001)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -310,6 +349,7 @@ def main():
         "linear_TOPS": round(gemm_ops / ((ms["act"] + ms["gemm"]) * 1e-3) / 1e12, 2),
         "kernel_ms": {n: round(v, 5) for n, v in ms.items()},
         "kernel_us_stats": stats_us,
+        "smi_clocks_during_timed_steps": clock_summary(clk),
         "int8_route": {"gemm_ms": round(int8_ms["gemm"], 5), "act_ms": round(int8_ms["act"], 5),
                        "gemm_TOPS": round(gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12, 2),
                        "pct_int8_peak": round(100.0 * gemm_ops / (int8_ms["gemm"] * 1e-3) / 1e12
