@@ -449,23 +449,52 @@ void w4a4_gemm_e3m2_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[i], Bt[j], acc[i][j], 0, 0, 0);
     }
   }
+  float bj[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (bias) {
+      if constexpr (PRE)
+        bj[j] = bf16_bits_to_float((uint16_t)*reinterpret_cast<const uint32_t*>(pb + kPreBiasOff + (wn * 64 + 32 * j + l32) * 4));
+      else
+        bj[j] = bf16_bits_to_float(bias[min(col0 + 32 * j + l32, No - 1)]);
+    }
+  }
+  if (m_tile + TM <= M && n_tile + TN <= N) {
+    // a whole tile (all but the ragged edge): no per-element bounds, one uniform base and
+    // fixed row offsets, and pairs of rows rounded to bf16 by one conversion (RNE)
+    const size_t base = (size_t)(m_tile + wm * 64) * N + n_tile + wn * 64;
+    const uint32_t lo = (uint32_t)(4 * hi) * (uint32_t)N + (uint32_t)l32;  // < 128 N
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {  // rows e and e + 1 are consecutive (e % 4 in {0, 2})
+          const uint32_t o = lo + (uint32_t)(32 * i + 8 * (e >> 2) + (e & 3)) * (uint32_t)N + 32 * j;
+          const float v0 = acc[i][j][e] + bj[j], v1 = acc[i][j][e + 1] + bj[j];
+          if constexpr (OUT_FP32) {
+            float* y = reinterpret_cast<float*>(Y) + base;
+            y[o] = v0;
+            y[o + (uint32_t)N] = v1;
+          } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(Y) + base;
+            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{v0, v1}), v2bf));
+            y[o] = (uint16_t)w;
+            y[o + (uint32_t)N] = (uint16_t)(w >> 16);
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = col0 + 32 * j + l32;
-    float bj = 0.0f;
-    if (bias) {
-      if constexpr (PRE)
-        bj = bf16_bits_to_float((uint16_t)*reinterpret_cast<const uint32_t*>(pb + kPreBiasOff + (wn * 64 + 32 * j + l32) * 4));
-      else
-        bj = bf16_bits_to_float(bias[min(col, No - 1)]);
-    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = row0 + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
         if (row < Mo && col < No) {
-          const float v = acc[i][j][e] + bj;
+          const float v = acc[i][j][e] + bj[j];
           if constexpr (OUT_FP32)
             reinterpret_cast<float*>(Y)[(size_t)row * No + col] = v;
           else
