@@ -278,17 +278,46 @@ void w4a4_gemm_kernel(
       }
     }
   }
+  float bj[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    bj[j] = bias ? bf16_bits_to_float(bias[min(col0 + 16 * j + rl, No - 1)]) : 0.0f;
+  if (m_tile + TM <= M && n_tile + TN <= N) {
+    // a whole tile (all but the ragged edge): no per-element bounds, one uniform base and
+    // fixed row offsets, and pairs of rows rounded to bf16 by one conversion (RNE)
+    const size_t base = (size_t)(m_tile + wm * WM) * N + n_tile + wn * WN;
+    const uint32_t lo = (uint32_t)(4 * kc) * (uint32_t)N + (uint32_t)rl;  // < TM N
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const uint32_t o = lo + (uint32_t)(16 * i + e) * (uint32_t)N + 16 * j;
+          const float v0 = acc[i][j][e] + bj[j], v1 = acc[i][j][e + 1] + bj[j];
+          if constexpr (OUT_FP32) {
+            float* y = reinterpret_cast<float*>(Y) + base;
+            y[o] = v0;
+            y[o + (uint32_t)N] = v1;
+          } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(Y) + base;
+            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{v0, v1}), v2bf));
+            y[o] = (uint16_t)w;
+            y[o + (uint32_t)N] = (uint16_t)(w >> 16);
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = col0 + 16 * j + rl;
-    const float bj = bias ? bf16_bits_to_float(bias[min(col, No - 1)]) : 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = row0 + 16 * i + 4 * kc + e;
         if (row < Mo && col < No) {
-          const float v = acc[i][j][e] + bj;
+          const float v = acc[i][j][e] + bj[j];
           if constexpr (OUT_FP32)
             reinterpret_cast<float*>(Y)[(size_t)row * No + col] = v;
           else
