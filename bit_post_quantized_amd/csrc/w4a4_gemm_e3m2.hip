@@ -263,9 +263,9 @@ void w4a4_gemm_e3m2_kernel(
     v8i A[2], B[2];
     v4h SA[2], SB[2];
   };
-  auto read_frag = [&](const uint8_t* st, int gg, Frag& F) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  // operands of 32-row tile pair i (A, B, s_x, s_w of tiles i) of group gg
+  auto read_half = [&](const uint8_t* st, int gg, int i, Frag& F) {
+    {
       const v2u* pa = reinterpret_cast<const v2u*>(st + a_base[i] + gg * kFrag);
       const v2u* pb = reinterpret_cast<const v2u*>(st + b_base[i] + gg * kFrag);
       const v2u a0 = pa[0], a1 = pa[1], a2 = pa[2];
@@ -279,6 +279,10 @@ void w4a4_gemm_e3m2_kernel(
         F.SB[i] = __builtin_bit_cast(v4h, v2u{sw & sb_keep, 0u});
       }
     }
+  };
+  auto read_frag = [&](const uint8_t* st, int gg, Frag& F) {
+    read_half(st, gg, 0, F);
+    read_half(st, gg, 1, F);
   };
   auto fma8 = [](v16f& a, const v16f& p, const v16f& sp, int half) {
 #pragma unroll
@@ -360,7 +364,7 @@ void w4a4_gemm_e3m2_kernel(
           __builtin_amdgcn_sched_barrier(0);
           if (ISSUE && li < kLoads) issue_load(s + 2, R2, li);
           // (also in a last stage without a second group: its LDS holds a valid duplicate)
-          if (t == 0 && gg + 1 < KS) read_frag(st, gg + 1, F[gg + 1]);
+          if (t < 2 && gg + 1 < KS) read_half(st, gg + 1, t, F[gg + 1]);
           // the pending tile: (1, 1) of the previous group at t == 0, else tile t - 1
           const int pi = t == 0 ? 1 : (t - 1) >> 1, pj = t == 0 ? 1 : (t - 1) & 1;
           const bool have = t > 0 || gg > 0;
@@ -378,8 +382,8 @@ void w4a4_gemm_e3m2_kernel(
           // registers stay distinct from tile t's, and each MFMA runs under the work behind it
           // (the scale product first measured 1 % faster than the partial first)
           if (ISSUE && li < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          if (t == 0 && gg + 1 < KS)  // the next group's operand reads go under this MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+          if (t < 2 && gg + 1 < KS)  // the next group's operand reads go under this MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
