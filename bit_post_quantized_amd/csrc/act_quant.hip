@@ -29,11 +29,14 @@
 namespace svdq {
 
 constexpr int kActRows = 16;    // tokens per workgroup
-constexpr int kActBatch = 3;    // groups per wave whose code loads are in flight together
-// up to 16 waves (4 per SIMD at <= 128 VGPRs) share a workgroup's groups: at K = 3072 each
-// takes one batch of 3; 8 waves of 6 groups hid less latency (27.3 against 25.6 us at
-// 4608 x 3072)
-constexpr int kActMaxWaves = 16;
+// Waves per workgroup and groups per wave whose code loads are in flight together, by the
+// rank's 16-wide tiles NTR.  Up to rank 32, 16 waves (4 per SIMD, <= 128 VGPRs) share a
+// workgroup's groups, at K = 3072 one batch of 3 each (8 waves of 6 groups hid less latency:
+// 27.3 against 25.6 us at 4608 x 3072).  Larger ranks (LoRA adapters) hold more low-rank
+// operands and accumulators than 128 VGPRs: 8 waves (<= 256 VGPRs) of 6 groups, and from
+// rank 112 on, batches of 3 (no spills at any rank).
+constexpr int act_max_waves(int ntr) { return ntr <= 2 ? 16 : 8; }
+constexpr int act_batch(int ntr) { return ntr <= 2 || ntr >= 7 ? 3 : 6; }
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
 // max over the four quarter lanes l, l ^ 16, l ^ 32, l ^ 48 of a row.  gfx950's permlane
@@ -50,7 +53,7 @@ __device__ __forceinline__ float max_row_quarters(float a) {
 
 // CODES: kCodesNibbles, kCodesBf6 (INT4 codes) or kCodesInt8 (8-bit codes of the W4A8 variant)
 template <int NTR, int CODES, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
-__global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
+__global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
     uint16_t* __restrict__ x_scales, float* __restrict__ T) {
@@ -95,6 +98,7 @@ __global__ __launch_bounds__(64 * kActMaxWaves) void quantize_act_kernel(
     }
   };
 
+  constexpr int kActBatch = act_batch(NTR);
   for (int j0 = wave; j0 < G; j0 += kActBatch * nwaves) {
     // every load of the batch is issued before any of it is used (group index clamped; a
     // clamped duplicate is computed but neither stored nor accumulated)
@@ -253,7 +257,8 @@ static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, c
                                    int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                                    hipStream_t stream) {
   const int G = K / kGroup;
-  const int nwaves = G < kActMaxWaves ? G : kActMaxWaves;
+  const int maxw = act_max_waves(r / 16);
+  const int nwaves = G < maxw ? G : maxw;
   const size_t red = (size_t)nwaves * 16 * r * sizeof(float);
   const size_t lam = (size_t)K * sizeof(float);
   if (lam + red <= kActLdsLambda)
