@@ -150,8 +150,9 @@ def cpu_baseline(rows: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the linear layer and the "
+              "KV quantizer run on one device; sharding them across GPUs is not implemented.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
