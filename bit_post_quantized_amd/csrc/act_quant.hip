@@ -8,21 +8,24 @@
 // SVDQ / DCMP: the branch is fused so the activations are read from HBM once.
 //
 // Work decomposition.  A workgroup owns 16 tokens (rows) and all of K; its waves take the
-// 64-groups round-robin.  In a group, lane l holds row l % 16 and the 16 consecutive k
-// [16 q, 16 q + 16) of quarter q = l / 16: two 16-byte loads, so every load instruction reads
-// 16 rows x 64 contiguous bytes.  The loads of kActBatch groups are issued before any of them is
-// used; inv_lambda sits in LDS.  The group max is folded over the four quarter lanes of a row
-// with two VALU lane swaps; every lane then codes its 16 values (exact quotient, no division per
-// element) as biased bytes c + 2^(b-1) and writes them in one of three containers: 8 bytes of
+// 64-groups round-robin.  In a group, lane l holds row l / 4 and the 16 consecutive k
+// [16 q, 16 q + 16) of quarter q = l % 4: two 16-byte loads, and the four lanes of a quad read
+// one row's 128 contiguous bytes.  (The vector memory unit resolves a 16-byte load four lanes
+// at a time; with the four lanes of a quad on four different rows, the same loads took twice
+// as long.)  The loads of kActBatch groups are issued before any of them is used; inv_lambda
+// sits in LDS.  The group max is folded over the quad with two DPP lane swaps; every lane then
+// codes its 16 values (exact quotient, no division per element) as biased bytes c + 2^(b-1)
+// and writes them in one of three containers: 8 bytes of
 // nibbles, 12 bytes of BF6 (E3M2) patterns into the tiled container (its row block, group,
 // slot row % 32 + 32 (q / 2), byte 12 (q % 2)), or 16 bytes of int8.  The quarter-0 lanes write
 // the 16 rows' scales.  For the tiled container the grid also covers the rows up to the next
 // multiple of 32, whose codes it writes as zeros.
-// Low-rank branch: the same registers rounded to bf16 are the A operand of two
-// v_mfma_f32_16x16x32_bf16 per group (k-slots 8 (l / 16) + i of the MFMA take k = 16 q + i and
-// 16 q + 8 + i), and L1, stored K-contiguous, is loaded with the same k map, so the MFMAs sum
-// exactly the group's 64 k.  Per-wave partial T tiles are summed in LDS in wave order
-// (deterministic) and written once.
+// Low-rank branch: the same registers rounded to bf16, and L1 (stored K-contiguous, loaded
+// with the same quad-per-row map: rank row 16 t + l / 4, quarter l % 4), are moved by a fixed
+// lane permutation (ds_bpermute: lane l takes lane 4 (l % 16) + l / 16) into the operand
+// layout of v_mfma_f32_16x16x32_bf16, row or column l % 16 and k-slots 8 (l / 16) + i; two
+// MFMAs per group take k = 16 q + i and 16 q + 8 + i, so they sum exactly the group's 64 k.
+// Per-wave partial T tiles are summed in LDS in wave order (deterministic) and written once.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
@@ -31,24 +34,30 @@ namespace svdq {
 constexpr int kActRows = 16;    // tokens per workgroup
 // Waves per workgroup and groups per wave whose code loads are in flight together, by the
 // rank's 16-wide tiles NTR.  Up to rank 32, 16 waves (4 per SIMD, <= 128 VGPRs) share a
-// workgroup's groups, at K = 3072 one batch of 3 each (8 waves of 6 groups hid less latency:
-// 27.3 against 25.6 us at 4608 x 3072).  Larger ranks (LoRA adapters) hold more low-rank
+// workgroup's groups, at K = 3072 one batch of 3 each (8 waves of 6 groups hid less latency).
+// Larger ranks (LoRA adapters) hold more low-rank
 // operands and accumulators than 128 VGPRs: 8 waves (<= 256 VGPRs) of 6 groups, and from
-// rank 112 on, batches of 3 (no spills at any rank).
+// rank 96 on, batches of 3 (no spills at any rank).
 constexpr int act_max_waves(int ntr) { return ntr <= 2 ? 16 : 8; }
-constexpr int act_batch(int ntr) { return ntr <= 2 || ntr >= 7 ? 3 : 6; }
+constexpr int act_batch(int ntr) { return ntr <= 2 || ntr >= 6 ? 3 : 6; }
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
-// max over the four quarter lanes l, l ^ 16, l ^ 32, l ^ 48 of a row.  gfx950's permlane
-// swaps exchange 16-lane rows (0 <-> 1, 2 <-> 3) and 32-lane halves between two registers in
-// the VALU; given the same value twice, the two results of a swap hold a lane's own value and
-// its partner's in some order, so their max is the pair's max (no LDS round trip, as a
-// ds_bpermute shuffle would take).
+// max over the four lanes of a quad (one row): DPP quad permutations [1, 0, 3, 2] and
+// [2, 3, 0, 1] bring each lane its neighbours' values within the VALU.
 __device__ __forceinline__ float max_row_quarters(float a) {
-  const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  a = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
-  const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  return __builtin_fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+  const float b = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(a), 0xB1, 0xF, 0xF, false));
+  a = __builtin_fmaxf(a, b);
+  const float c = __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(a), 0x4E, 0xF, 0xF, false));
+  return __builtin_fmaxf(a, c);
+}
+
+// the fixed lane permutation into the MFMA operand layout: each lane takes the dwords of the
+// lane whose byte address src_byte gives (4 (4 (l % 16) + l / 16) for lane l)
+__device__ __forceinline__ v4u quad_to_mfma(v4u v, int src_byte) {
+  return v4u{(uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.x),
+             (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.y),
+             (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.z),
+             (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.w)};
 }
 
 // CODES: kCodesNibbles, kCodesBf6 (INT4 codes) or kCodesInt8 (8-bit codes of the W4A8 variant)
@@ -63,12 +72,13 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  const int rl = lane & 15;
-  const int q = lane >> 4;
+  const int rl = lane >> 2;  // this lane's row of the block
+  const int q = lane & 3;    // and quarter of the group
+  const int src_byte = 4 * (4 * (lane & 15) + (lane >> 4));  // the MFMA layout's source lane
+  const int G = K / kGroup;
   const int row0 = blockIdx.x * kActRows;
   const int row = row0 + rl;
   const int row_ld = row < M ? row : M - 1;
-  const int G = K / kGroup;
   const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
   float* lam = smem;
   float* red = smem + (LAM_LDS ? K : 0);
@@ -86,7 +96,8 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's L1 operands for group g (k = 16 q .. 16 q + 15 of rank rows 16 t + rl)
+  // this lane's L1 values for group g (k = 16 q .. 16 q + 15 of rank rows 16 t + rl), in the
+  // load layout
   auto load_l1 = [&](int g, v4u (&dst)[NT][2]) {
     if constexpr (NTR > 0) {
 #pragma unroll
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
 #pragma unroll
     for (int b = 0; b < kActBatch; ++b) {
       const int g_raw = j0 + b * nwaves;
-      const bool gv = g_raw < G;  // uniform over the workgroup
+      const bool gv = g_raw < G;  // uniform over the wave
       const int g = gv ? g_raw : G - 1;
       if (b + 1 < kActBatch) load_l1(min(j0 + (b + 1) * nwaves, G - 1), bfr[(b + 1) & 1]);
       const int k0 = g * kGroup + 16 * q;
@@ -189,12 +200,15 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
 
       // ---- low-rank down-projection on bf16 MFMA (a clamped duplicate group adds zero)
       if constexpr (NTR > 0) {
-        v8bf a0 = to_bf16x8(xh), a1 = to_bf16x8(xh + 8);
+        v8bf a0 = __builtin_bit_cast(v8bf, quad_to_mfma(__builtin_bit_cast(v4u, to_bf16x8(xh)), src_byte));
+        v8bf a1 = __builtin_bit_cast(v8bf, quad_to_mfma(__builtin_bit_cast(v4u, to_bf16x8(xh + 8)), src_byte));
         if (!gv) a0 = a1 = v8bf{};
 #pragma unroll
         for (int t = 0; t < NTR; ++t) {
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, bfr[b & 1][t][0]), acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, bfr[b & 1][t][1]), acc[t], 0, 0, 0);
+          const v8bf b0 = __builtin_bit_cast(v8bf, quad_to_mfma(bfr[b & 1][t][0], src_byte));
+          const v8bf b1 = __builtin_bit_cast(v8bf, quad_to_mfma(bfr[b & 1][t][1], src_byte));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
         }
       }
     }
@@ -206,7 +220,7 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
     for (int t = 0; t < NTR; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        red[((size_t)wave * 16 + 4 * q + i) * r + t * 16 + rl] = acc[t][i];
+        red[((size_t)wave * 16 + 4 * (lane >> 4) + i) * r + t * 16 + (lane & 15)] = acc[t][i];
     __syncthreads();
     for (int idx = threadIdx.x; idx < 16 * r; idx += blockDim.x) {
       const int rr = idx / r;
