@@ -284,7 +284,8 @@ void w4a4_gemm_kernel(
     bj[j] = bias ? bf16_bits_to_float(bias[min(col0 + 16 * j + rl, No - 1)]) : 0.0f;
   if (m_tile + TM <= M && n_tile + TN <= N) {
     // a whole tile (all but the ragged edge): no per-element bounds, one uniform base and
-    // fixed row offsets, and pairs of rows rounded to bf16 by one conversion (RNE)
+    // fixed row offsets, and pairs of rows rounded to bf16 by one conversion (RNE); Y is
+    // written once, with non-temporal stores
     const size_t base = (size_t)(m_tile + wm * WM) * N + n_tile + wn * WN;
     const uint32_t lo = (uint32_t)(4 * kc) * (uint32_t)N + (uint32_t)rl;  // < TM N
 #pragma unroll
@@ -297,13 +298,13 @@ void w4a4_gemm_kernel(
           const float v0 = acc[i][j][e] + bj[j], v1 = acc[i][j][e + 1] + bj[j];
           if constexpr (OUT_FP32) {
             float* y = reinterpret_cast<float*>(Y) + base;
-            y[o] = v0;
-            y[o + (uint32_t)N] = v1;
+            __builtin_nontemporal_store(v0, y + o);
+            __builtin_nontemporal_store(v1, y + o + (uint32_t)N);
           } else {
             uint16_t* y = reinterpret_cast<uint16_t*>(Y) + base;
             const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{v0, v1}), v2bf));
-            y[o] = (uint16_t)w;
-            y[o + (uint32_t)N] = (uint16_t)(w >> 16);
+            __builtin_nontemporal_store((uint16_t)w, y + o);
+            __builtin_nontemporal_store((uint16_t)(w >> 16), y + o + (uint32_t)N);
           }
         }
     return;
