@@ -415,27 +415,31 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
     mine[kFusedCh + tid] = phi;
   }
   __syncthreads();
-  if (tid == 0) {
-    __hip_atomic_store(tags + slab * kFusedParts + part, epoch, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 64) {  // wave 0: lane p < kFusedParts watches part p's tag
+    if (tid == 0)
+      __hip_atomic_store(tags + slab * kFusedParts + part, epoch, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
     int fb = 0;
     const long long start = wall_clock64();
-    // relaxed polling (an acquire per poll would invalidate caches on every iteration); the
-    // acquire fence after the wait orders the reads of the partial ranges
-    for (int p = 0; p < kFusedParts && !fb; ++p) {
-      while (__hip_atomic_load(tags + slab * kFusedParts + p, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-        if (wall_clock64() - start > spin_ticks) {
-          fb = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    // relaxed polling of all the tags at once, one round trip per poll (an acquire per poll
+    // would invalidate caches on every iteration; tags polled one after the other cost one
+    // round trip each: 4.8 us from the slowest part's publication to the exchange's end);
+    // the acquire fence after the wait orders the reads of the partial ranges
+    for (;;) {
+      const bool seen = tid >= kFusedParts ||
+                        __hip_atomic_load(tags + slab * kFusedParts + tid, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      if (__all(seen)) break;  // uniform over the wave
+      if (wall_clock64() - start > spin_ticks) {
+        fb = 1;
+        break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
     // one acquire (it invalidates the CU's vector cache, which every wave shares) before the
     // barrier after which the partial ranges are read
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    fallback = fb;
+    if (tid == 0) fallback = fb;
   }
   __syncthreads();
   if (!fallback) {
