@@ -275,10 +275,13 @@ def _gpu_kv(x_bits):
     return q.cpu().numpy(), s.cpu().numpy(), z.cpu().numpy(), host_u16(out)
 
 
-# (None,)*3 is the full cache [10240, 32, 128]; 1000 and 100 tokens end in a partial 64-token
-# range chunk; 12800 tokens fill 200 chunks; (1, 2, 8) is a single token of 16 channels
+# (None,)*3 is the full cache [10240, 32, 128] (single pass, 32 slabs of 128 channels);
+# (2000, 16, 128) is a single pass over 16 slabs, (1000, 8, 64) over 4 and (300, 3, 128) over 3;
+# 1000 and 100 tokens end in a partial 64-token range chunk of the three-pass schedule; 12800
+# tokens (three passes) fill 200 chunks; (1, 2, 8) is a single token of 16 channels; (5, 2, 128)
+# is a single pass whose token parts are mostly empty
 @pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64),
-                                   (12800, 32, 128)])
+                                   (2000, 16, 128), (5, 2, 128), (300, 3, 128), (12800, 32, 128)])
 def test_kv_quant_dequant_bitexact(gpu_lib, shape):
     for name, (x, ref) in kv_case(*shape).items():
         q, s, z, xo = _gpu_kv(x)
@@ -304,10 +307,10 @@ def test_kv_workspace_needs_no_initialization_and_is_reusable(gpu_lib):
         np.testing.assert_array_equal(z.cpu().numpy(), ref["zero"])
 
 
-@pytest.mark.parametrize("shape", [(1000, 8, 64), (10240, 32, 128), (5, 1, 64)])
+@pytest.mark.parametrize("shape", [(1000, 8, 64), (10240, 32, 128), (5, 2, 128)])
 def test_kv_single_pass_self_contained_path(gpu_lib, shape, monkeypatch):
     """The single-pass quantizer with its bounded wait forced to time out at once: every block
-    computes its slab's range from x itself.  Same codes as the oracle; (5, 1, 64) has token
+    computes its slabs' ranges from x itself.  Same codes as the oracle; (5, 2, 128) has token
     parts that are empty."""
     monkeypatch.setenv("SVDQ_KV_SPIN_TICKS", "0")
     for name, (x, ref) in kv_case(*shape).items():
