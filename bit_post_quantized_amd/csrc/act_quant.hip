@@ -33,12 +33,14 @@ namespace svdq {
 
 constexpr int kActRows = 16;    // tokens per workgroup
 // Waves per workgroup and groups per wave whose code loads are in flight together, by the
-// rank's 16-wide tiles NTR.  Up to rank 32, 16 waves (4 per SIMD, <= 128 VGPRs) share a
-// workgroup's groups, at K = 3072 one batch of 3 each (8 waves of 6 groups hid less latency).
-// Larger ranks (LoRA adapters) hold more low-rank
-// operands and accumulators than 128 VGPRs: 8 waves (<= 256 VGPRs) of 6 groups, and from
-// rank 96 on, batches of 3 (no spills at any rank).
-constexpr int act_max_waves(int ntr) { return ntr <= 2 ? 16 : 8; }
+// rank's 16-wide tiles NTR.  Eight waves share a workgroup's groups.  Up to rank 32 they stay
+// within 128 VGPRs, so two workgroups share a CU and a 4608-row pass (288 workgroups) is
+// resident at once: 16 waves per workgroup (one workgroup per CU, 256 in a first round and 32
+// in a second) took 23.2 against 20.9 us inside the bench step.  At K = 3072 each wave takes
+// two batches of 3 groups.  Larger ranks (LoRA adapters) hold more low-rank operands and
+// accumulators (<= 256 VGPRs): batches of 6 groups, and from rank 96 on, batches of 3 (no
+// spills at any rank).
+constexpr int act_max_waves(int) { return 8; }
 constexpr int act_batch(int ntr) { return ntr <= 2 || ntr >= 6 ? 3 : 6; }
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
