@@ -25,7 +25,7 @@
 // channel's reciprocal (div_rn), then rne, + z and the clamp: no division per element, no branch.
 //
 // kv_dequant_kernel writes x' = bf16(fl32((q - z) * s)) (v_cvt_pk_bf16_f32 rounds to nearest
-// even) with the quantize pass's tiling.
+// even): blocks of 512 channels x 32 tokens, each lane 8 channels of 8 rows.
 //
 // The fused pass and the dequantization touch each byte once: their loads and stores are
 // non-temporal, so the streams pass the caches without displacing other data.  A plain read
@@ -48,6 +48,11 @@ constexpr int kKvWaves = 4;
 constexpr int kKvBatch = 16;                               // rows in flight per lane
 constexpr int kKvTokPerBlockQ = kKvWaves * kKvBatch;       // 64
 constexpr int kRangeTokPerBlock = kKvTokPerBlockQ;         // one partial range per 64 tokens
+// dequantization: 8 rows in flight per lane, so a block covers 512 channels x 32 tokens (16
+// rows per lane and 64 tokens per block took 26.1 against 24.9 us per tensor in the bench step;
+// 32 rows 30.4)
+constexpr int kDeqBatch = 8;
+constexpr int kDeqTokPerBlock = kKvWaves * kDeqBatch;      // 32
 // parameter fold: a block of 256 threads folds 32 channels; 8 threads per channel split the chunks
 constexpr int kFoldChannels = 32;
 constexpr int kFoldSplit = 8;
@@ -261,8 +266,8 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kKvSlab + lane * kKvLanesC;
   if (c0 >= channels) return;
-  const int t_begin = blockIdx.y * kKvTokPerBlockQ + wave * kKvBatch;
-  const int t_end = min(tokens, t_begin + kKvBatch);
+  const int t_begin = blockIdx.y * kDeqTokPerBlock + wave * kDeqBatch;
+  const int t_end = min(tokens, t_begin + kDeqBatch);
   float s[8], z[8];
   load_params8(scale, zero, c0, s, z);
   const uint8_t* p = q + (size_t)c0;
@@ -284,12 +289,12 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restri
     return v4u{o[0], o[1], o[2], o[3]};
   };
   int t = t_begin;
-  for (; t + kKvBatch <= t_end; t += kKvBatch) {
-    v2u w[kKvBatch];
+  for (; t + kDeqBatch <= t_end; t += kDeqBatch) {
+    v2u w[kDeqBatch];
 #pragma unroll
-    for (int b = 0; b < kKvBatch; ++b) w[b] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p + (size_t)(t + b) * channels));
+    for (int b = 0; b < kDeqBatch; ++b) w[b] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p + (size_t)(t + b) * channels));
 #pragma unroll
-    for (int b = 0; b < kKvBatch; ++b) __builtin_nontemporal_store(dequant_row(w[b]), reinterpret_cast<v4u*>(d + (size_t)(t + b) * channels));
+    for (int b = 0; b < kDeqBatch; ++b) __builtin_nontemporal_store(dequant_row(w[b]), reinterpret_cast<v4u*>(d + (size_t)(t + b) * channels));
   }
   for (; t < t_end; ++t)
     *reinterpret_cast<v4u*>(d + (size_t)t * channels) = dequant_row(*reinterpret_cast<const v2u*>(p + (size_t)t * channels));
@@ -613,7 +618,7 @@ hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t*
 
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,
                              int tokens, int channels, uint16_t* x_out, hipStream_t stream) {
-  const dim3 grid(kv_slabs(channels), (tokens + kKvTokPerBlockQ - 1) / kKvTokPerBlockQ);
+  const dim3 grid(kv_slabs(channels), (tokens + kDeqTokPerBlock - 1) / kDeqTokPerBlock);
   hipLaunchKernelGGL(kv_dequant_kernel, grid, dim3(256), 0, stream, q, scale, zero, tokens,
                      channels, x_out);
   return hipGetLastError();
