@@ -72,20 +72,50 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError("libsvdq takes device tensors")
-    if not t.is_contiguous():
-        raise ValueError("libsvdq takes contiguous tensors")
-    return t.data_ptr()
+class _Args:
+    """Checks one call's tensors before their pointers go to the library: each must be a
+    contiguous device tensor on the same device as the others, holding at least the bytes the
+    call reads or writes through it. The library cannot see buffer sizes, so a short buffer
+    would otherwise be read or written past its end. None passes through as NULL, which the
+    library rejects where the argument is required."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.device: Optional[torch.device] = None
+
+    def __call__(self, t: Optional[torch.Tensor], need: int, name: str):
+        if t is None:
+            return None
+        if not t.is_cuda:
+            raise ValueError(f"{self.fn}: {name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.fn}: {name} must be contiguous")
+        if self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            raise ValueError(f"{self.fn}: {name} is on {t.device}, "
+                             f"other arguments on {self.device}")
+        have = t.numel() * t.element_size()
+        if have < need:
+            raise ValueError(f"{self.fn}: {name} holds {have} bytes, the call needs {need}")
+        return t.data_ptr()
+
+    def stream(self, stream) -> Optional[int]:
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def _stream(stream) -> Optional[int]:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+def _out_dtype(fn: str, Y: torch.Tensor) -> int:
+    if Y.dtype == torch.float32:
+        return SVDQ_OUT_FP32
+    if Y.dtype == torch.bfloat16:
+        return SVDQ_OUT_BF16
+    raise ValueError(f"{fn}: Y must be bfloat16 or float32 (got {Y.dtype})")
+
+
+def _e3m2_bytes(rows: int, K: int) -> int:
+    return load().svdq_e3m2_bytes(rows, K) if rows > 0 else 0
 
 
 def _check(fn: str, status: int) -> None:
@@ -102,9 +132,12 @@ def svdq_abi_version() -> int:
 def svdq_pack_weights(R: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor,
                       stream=None) -> None:
     """R fp32 [K, N] -> wq uint8 [N, K/2], w_scales fp16 [K/64, N]."""
+    fn = "svdq_pack_weights"
     K, N = R.shape
-    _check("svdq_pack_weights", load().svdq_pack_weights(
-        _ptr(R), K, N, _ptr(wq), _ptr(w_scales), _stream(stream)))
+    a = _Args(fn)
+    args = (a(R, 4 * K * N, "R"), K, N, a(wq, N * (K // 2), "wq"),
+            a(w_scales, 2 * (K // 64) * N, "w_scales"))
+    _check(fn, load().svdq_pack_weights(*args, a.stream(stream)))
 
 
 def svdq_quantize_act(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[torch.Tensor],
@@ -112,10 +145,37 @@ def svdq_quantize_act(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[to
                       T: Optional[torch.Tensor], stream=None) -> None:
     """X bf16 [M, K], inv_lambda fp32 [K], L1 bf16 [r, K] (K-contiguous) ->
     xq uint8 [M, K/2], x_scales fp16 [K/64, M], T fp32 [M, r]."""
+    _quantize_act("svdq_quantize_act", X, inv_lambda, L1, r, xq, "xq",
+                  X.shape[0] * (X.shape[1] // 2), x_scales, T, stream)
+
+
+def _quantize_act(fn, X, inv_lambda, L1, r, codes, code_name, code_bytes, x_scales, T,
+                  stream) -> None:
     M, K = X.shape
-    _check("svdq_quantize_act", load().svdq_quantize_act(
-        _ptr(X), _ptr(inv_lambda), _ptr(L1), M, K, r, _ptr(xq), _ptr(x_scales), _ptr(T),
-        _stream(stream)))
+    a = _Args(fn)
+    args = (a(X, 2 * M * K, "X"), a(inv_lambda, 4 * K, "inv_lambda"), a(L1, 2 * r * K, "L1"),
+            M, K, r, a(codes, code_bytes, code_name), a(x_scales, 2 * (K // 64) * M, "x_scales"),
+            a(T, 4 * M * r, "T"))
+    _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
+
+
+def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L2, bias, M, N,
+          K, r, Y, stream) -> None:
+    out = _out_dtype(fn, Y)
+    a = _Args(fn)
+    G = K // 64
+    args = (a(xq, x_bytes, x_name), a(x_scales, 2 * G * M, "x_scales"),
+            a(T, 4 * M * r, "T"), a(wq, w_bytes, w_name),
+            a(w_scales, 2 * G * N, "w_scales"), a(L2, 2 * r * N, "L2"), a(bias, 2 * N, "bias"),
+            M, N, K, r, a(Y, Y.element_size() * M * N, "Y"), out)
+    _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
+
+
+def _partials(fn, xq, x_name, x_bytes, wq, w_name, w_bytes, M, N, K, P, stream) -> None:
+    a = _Args(fn)
+    args = (a(xq, x_bytes, x_name), a(wq, w_bytes, w_name), M, N, K,
+            a(P, 4 * (K // 64) * M * N, "P"))
+    _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
 def svdq_w4a4_gemm(xq: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
@@ -124,10 +184,8 @@ def svdq_w4a4_gemm(xq: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.T
     """Y [M, N] (bf16 or fp32, chosen by Y's dtype) of the fused W4A4 + low-rank GEMM."""
     M, half_k = xq.shape
     N = wq.shape[0]
-    out = SVDQ_OUT_FP32 if Y.dtype == torch.float32 else SVDQ_OUT_BF16
-    _check("svdq_w4a4_gemm", load().svdq_w4a4_gemm(
-        _ptr(xq), _ptr(x_scales), _ptr(T), _ptr(wq), _ptr(w_scales), _ptr(L2), _ptr(bias),
-        M, N, 2 * half_k, r, _ptr(Y), out, _stream(stream)))
+    _gemm("svdq_w4a4_gemm", xq, "xq", M * half_k, x_scales, T, wq, "wq", N * half_k, w_scales,
+          L2, bias, M, N, 2 * half_k, r, Y, stream)
 
 
 def svdq_w4a4_partials(xq: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
@@ -135,8 +193,8 @@ def svdq_w4a4_partials(xq: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
     """P int32 [K/64, M, N]: the exact group partials of the GEMM's inner loop."""
     M, half_k = xq.shape
     N = wq.shape[0]
-    _check("svdq_w4a4_partials", load().svdq_w4a4_partials(
-        _ptr(xq), _ptr(wq), M, N, 2 * half_k, _ptr(P), _stream(stream)))
+    _partials("svdq_w4a4_partials", xq, "xq", M * half_k, wq, "wq", N * half_k, M, N,
+              2 * half_k, P, stream)
 
 
 def svdq_e3m2_bytes(rows: int, K: int) -> int:
@@ -147,9 +205,12 @@ def svdq_e3m2_bytes(rows: int, K: int) -> int:
 def svdq_pack_weights_e3m2(R: torch.Tensor, wq6: torch.Tensor, w_scales: torch.Tensor,
                            stream=None) -> None:
     """R fp32 [K, N] -> wq6 (tiled BF6 container, svdq_e3m2_bytes(N, K) bytes), w_scales."""
+    fn = "svdq_pack_weights_e3m2"
     K, N = R.shape
-    _check("svdq_pack_weights_e3m2", load().svdq_pack_weights_e3m2(
-        _ptr(R), K, N, _ptr(wq6), _ptr(w_scales), _stream(stream)))
+    a = _Args(fn)
+    args = (a(R, 4 * K * N, "R"), K, N, a(wq6, _e3m2_bytes(N, K), "wq6"),
+            a(w_scales, 2 * (K // 64) * N, "w_scales"))
+    _check(fn, load().svdq_pack_weights_e3m2(*args, a.stream(stream)))
 
 
 def svdq_quantize_act_e3m2(X: torch.Tensor, inv_lambda: torch.Tensor,
@@ -157,10 +218,8 @@ def svdq_quantize_act_e3m2(X: torch.Tensor, inv_lambda: torch.Tensor,
                            x_scales: torch.Tensor, T: Optional[torch.Tensor],
                            stream=None) -> None:
     """As svdq_quantize_act with the codes written to xq6, the tiled BF6 container of M rows."""
-    M, K = X.shape
-    _check("svdq_quantize_act_e3m2", load().svdq_quantize_act_e3m2(
-        _ptr(X), _ptr(inv_lambda), _ptr(L1), M, K, r, _ptr(xq6), _ptr(x_scales), _ptr(T),
-        _stream(stream)))
+    _quantize_act("svdq_quantize_act_e3m2", X, inv_lambda, L1, r, xq6, "xq6",
+                  _e3m2_bytes(X.shape[0], X.shape[1]), x_scales, T, stream)
 
 
 def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
@@ -171,39 +230,51 @@ def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[t
     w_scales [K/64, N])."""
     G, M = x_scales.shape
     N = w_scales.shape[1]
-    out = SVDQ_OUT_FP32 if Y.dtype == torch.float32 else SVDQ_OUT_BF16
-    _check("svdq_w4a4_gemm_e3m2", load().svdq_w4a4_gemm_e3m2(
-        _ptr(xq6), _ptr(x_scales), _ptr(T), _ptr(wq6), _ptr(w_scales), _ptr(L2), _ptr(bias),
-        M, N, 64 * G, r, _ptr(Y), out, _stream(stream)))
+    K = 64 * G
+    _gemm("svdq_w4a4_gemm_e3m2", xq6, "xq6", _e3m2_bytes(M, K), x_scales, T, wq6, "wq6",
+          _e3m2_bytes(N, K), w_scales, L2, bias, M, N, K, r, Y, stream)
 
 
 def svdq_w4a4_partials_e3m2(xq6: torch.Tensor, wq6: torch.Tensor, M: int, N: int, K: int,
                             P: torch.Tensor, stream=None) -> None:
     """P int32 [K/64, M, N]: the exact group partials of the BF6 GEMM's inner loop."""
-    _check("svdq_w4a4_partials_e3m2", load().svdq_w4a4_partials_e3m2(
-        _ptr(xq6), _ptr(wq6), M, N, K, _ptr(P), _stream(stream)))
+    _partials("svdq_w4a4_partials_e3m2", xq6, "xq6", _e3m2_bytes(M, K), wq6, "wq6",
+              _e3m2_bytes(N, K), M, N, K, P, stream)
 
 
 def kv_int8_workspace_bytes(tokens: int, channels: int) -> int:
     return load().kv_int8_workspace_bytes(tokens, channels)
 
 
+def _kv_shape(t: torch.Tensor):
+    tokens = t.shape[0]
+    channels = 1
+    for d in t.shape[1:]:
+        channels *= d
+    return tokens, channels
+
+
 def kv_int8_quant(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
                   workspace: Optional[torch.Tensor], stream=None) -> None:
     """x bf16 [tokens, ...] viewed as [tokens, channels] -> q uint8, scale fp32, zero uint8."""
-    tokens = x.shape[0]
-    channels = x.numel() // tokens if tokens else int(torch.tensor(x.shape[1:]).prod())
-    _check("kv_int8_quant", load().kv_int8_quant(
-        _ptr(x), tokens, channels, _ptr(q), _ptr(scale), _ptr(zero), _ptr(workspace),
-        _stream(stream)))
+    fn = "kv_int8_quant"
+    tokens, channels = _kv_shape(x)
+    a = _Args(fn)
+    args = (a(x, 2 * tokens * channels, "x"), tokens, channels, a(q, tokens * channels, "q"),
+            a(scale, 4 * channels, "scale"), a(zero, channels, "zero"),
+            a(workspace, kv_int8_workspace_bytes(tokens, channels) if tokens else 0, "workspace"))
+    _check(fn, load().kv_int8_quant(*args, a.stream(stream)))
 
 
 def kv_int8_dequant(q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
                     x_out: torch.Tensor, stream=None) -> None:
-    tokens = q.shape[0]
-    channels = q.numel() // tokens if tokens else int(torch.tensor(q.shape[1:]).prod())
-    _check("kv_int8_dequant", load().kv_int8_dequant(
-        _ptr(q), _ptr(scale), _ptr(zero), tokens, channels, _ptr(x_out), _stream(stream)))
+    """q uint8 [tokens, ...] with its per-channel scale and zero -> x_out bf16, same shape."""
+    fn = "kv_int8_dequant"
+    tokens, channels = _kv_shape(q)
+    a = _Args(fn)
+    args = (a(q, tokens * channels, "q"), a(scale, 4 * channels, "scale"),
+            a(zero, channels, "zero"), tokens, channels, a(x_out, 2 * tokens * channels, "x_out"))
+    _check(fn, load().kv_int8_dequant(*args, a.stream(stream)))
 
 
 def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[torch.Tensor],
@@ -211,10 +282,8 @@ def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional
                          T: Optional[torch.Tensor], stream=None) -> None:
     """W4A8 activation pass: X bf16 [M, K] -> xq8 int8 [M, K], x_scales fp16 [K/64, M],
     T fp32 [M, r]."""
-    M, K = X.shape
-    _check("svdq_quantize_act_a8", load().svdq_quantize_act_a8(
-        _ptr(X), _ptr(inv_lambda), _ptr(L1), M, K, r, _ptr(xq8), _ptr(x_scales), _ptr(T),
-        _stream(stream)))
+    _quantize_act("svdq_quantize_act_a8", X, inv_lambda, L1, r, xq8, "xq8",
+                  X.shape[0] * X.shape[1], x_scales, T, stream)
 
 
 def svdq_w4a8_gemm(xq8: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
@@ -223,10 +292,8 @@ def svdq_w4a8_gemm(xq8: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.
     """Y [M, N] of the W4A8 GEMM: int8 activation codes xq8 [M, K], INT4 nibbles wq [N, K/2]."""
     M, K = xq8.shape
     N = wq.shape[0]
-    out = SVDQ_OUT_FP32 if Y.dtype == torch.float32 else SVDQ_OUT_BF16
-    _check("svdq_w4a8_gemm", load().svdq_w4a8_gemm(
-        _ptr(xq8), _ptr(x_scales), _ptr(T), _ptr(wq), _ptr(w_scales), _ptr(L2), _ptr(bias),
-        M, N, K, r, _ptr(Y), out, _stream(stream)))
+    _gemm("svdq_w4a8_gemm", xq8, "xq8", M * K, x_scales, T, wq, "wq", N * (K // 2), w_scales,
+          L2, bias, M, N, K, r, Y, stream)
 
 
 def svdq_w4a8_partials(xq8: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
@@ -234,8 +301,8 @@ def svdq_w4a8_partials(xq8: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
     """P int32 [K/64, M, N]: the exact group partials of the W4A8 GEMM's inner loop."""
     M, K = xq8.shape
     N = wq.shape[0]
-    _check("svdq_w4a8_partials", load().svdq_w4a8_partials(
-        _ptr(xq8), _ptr(wq), M, N, K, _ptr(P), _stream(stream)))
+    _partials("svdq_w4a8_partials", xq8, "xq8", M * K, wq, "wq", N * (K // 2), M, N, K, P,
+              stream)
 
 
 def kv_int8_attention_workspace_bytes(nq: int, tokens: int, heads: int, dim: int) -> int:
@@ -248,9 +315,14 @@ def kv_int8_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scale: torch.Ten
                       workspace: torch.Tensor, stream=None) -> None:
     """Decode attention over the INT8 cache: q bf16 [nq, heads, dim], codes uint8
     [tokens, heads * dim], per-channel scale / zero -> out bf16 [nq, heads, dim]."""
+    fn = "kv_int8_attention"
     nq, heads, dim = q.shape
     tokens = k_codes.shape[0]
-    _check("kv_int8_attention", load().kv_int8_attention(
-        _ptr(q), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes), _ptr(v_scale),
-        _ptr(v_zero), nq, tokens, heads, dim, float(sm_scale), _ptr(out), _ptr(workspace),
-        _stream(stream)))
+    C = heads * dim
+    ws = kv_int8_attention_workspace_bytes(nq, tokens, heads, dim) if nq and tokens else 0
+    a = _Args(fn)
+    args = (a(q, 2 * nq * C, "q"), a(k_codes, tokens * C, "k_codes"), a(k_scale, 4 * C, "k_scale"),
+            a(k_zero, C, "k_zero"), a(v_codes, tokens * C, "v_codes"),
+            a(v_scale, 4 * C, "v_scale"), a(v_zero, C, "v_zero"), nq, tokens, heads, dim,
+            float(sm_scale), a(out, 2 * nq * C, "out"), a(workspace, ws, "workspace"))
+    _check(fn, load().kv_int8_attention(*args, a.stream(stream)))
