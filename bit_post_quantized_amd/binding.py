@@ -72,22 +72,30 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+_BF16, _F16, _F32, _U8, _I8, _I32 = (torch.bfloat16, torch.float16, torch.float32, torch.uint8,
+                                     torch.int8, torch.int32)
+
+
 class _Args:
     """Checks one call's tensors before their pointers go to the library: each must be a
-    contiguous device tensor on the same device as the others, holding at least the bytes the
-    call reads or writes through it. The library cannot see buffer sizes, so a short buffer
-    would otherwise be read or written past its end. None passes through as NULL, which the
-    library rejects where the argument is required."""
+    contiguous device tensor of the layout's dtype, on the same device as the others, holding
+    at least the bytes the call reads or writes through it. The library cannot see buffer
+    sizes or dtypes, so a short buffer would otherwise be read or written past its end and a
+    wrong dtype read as other bits. None passes through as NULL, which the library rejects
+    where the argument is required. Workspaces are raw bytes of any dtype."""
 
     def __init__(self, fn: str):
         self.fn = fn
         self.device: Optional[torch.device] = None
 
-    def __call__(self, t: Optional[torch.Tensor], need: int, name: str):
+    def __call__(self, t: Optional[torch.Tensor], need: int, name: str,
+                 dtype: Optional[torch.dtype] = None):
         if t is None:
             return None
         if not t.is_cuda:
             raise ValueError(f"{self.fn}: {name} must be a device tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{self.fn}: {name} must be {dtype} (got {t.dtype})")
         if not t.is_contiguous():
             raise ValueError(f"{self.fn}: {name} must be contiguous")
         if self.device is None:
@@ -135,8 +143,8 @@ def svdq_pack_weights(R: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor,
     fn = "svdq_pack_weights"
     K, N = R.shape
     a = _Args(fn)
-    args = (a(R, 4 * K * N, "R"), K, N, a(wq, N * (K // 2), "wq"),
-            a(w_scales, 2 * (K // 64) * N, "w_scales"))
+    args = (a(R, 4 * K * N, "R", _F32), K, N, a(wq, N * (K // 2), "wq", _U8),
+            a(w_scales, 2 * (K // 64) * N, "w_scales", _F16))
     _check(fn, load().svdq_pack_weights(*args, a.stream(stream)))
 
 
@@ -153,9 +161,10 @@ def _quantize_act(fn, X, inv_lambda, L1, r, codes, code_name, code_bytes, x_scal
                   stream) -> None:
     M, K = X.shape
     a = _Args(fn)
-    args = (a(X, 2 * M * K, "X"), a(inv_lambda, 4 * K, "inv_lambda"), a(L1, 2 * r * K, "L1"),
-            M, K, r, a(codes, code_bytes, code_name), a(x_scales, 2 * (K // 64) * M, "x_scales"),
-            a(T, 4 * M * r, "T"))
+    args = (a(X, 2 * M * K, "X", _BF16), a(inv_lambda, 4 * K, "inv_lambda", _F32),
+            a(L1, 2 * r * K, "L1", _BF16), M, K, r,
+            a(codes, code_bytes, code_name, _I8 if code_name == "xq8" else _U8),
+            a(x_scales, 2 * (K // 64) * M, "x_scales", _F16), a(T, 4 * M * r, "T", _F32))
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
@@ -164,17 +173,18 @@ def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L
     out = _out_dtype(fn, Y)
     a = _Args(fn)
     G = K // 64
-    args = (a(xq, x_bytes, x_name), a(x_scales, 2 * G * M, "x_scales"),
-            a(T, 4 * M * r, "T"), a(wq, w_bytes, w_name),
-            a(w_scales, 2 * G * N, "w_scales"), a(L2, 2 * r * N, "L2"), a(bias, 2 * N, "bias"),
+    args = (a(xq, x_bytes, x_name, _I8 if x_name == "xq8" else _U8),
+            a(x_scales, 2 * G * M, "x_scales", _F16), a(T, 4 * M * r, "T", _F32),
+            a(wq, w_bytes, w_name, _U8), a(w_scales, 2 * G * N, "w_scales", _F16),
+            a(L2, 2 * r * N, "L2", _BF16), a(bias, 2 * N, "bias", _BF16),
             M, N, K, r, a(Y, Y.element_size() * M * N, "Y"), out)
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
 def _partials(fn, xq, x_name, x_bytes, wq, w_name, w_bytes, M, N, K, P, stream) -> None:
     a = _Args(fn)
-    args = (a(xq, x_bytes, x_name), a(wq, w_bytes, w_name), M, N, K,
-            a(P, 4 * (K // 64) * M * N, "P"))
+    args = (a(xq, x_bytes, x_name, _I8 if x_name == "xq8" else _U8),
+            a(wq, w_bytes, w_name, _U8), M, N, K, a(P, 4 * (K // 64) * M * N, "P", _I32))
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
@@ -208,8 +218,8 @@ def svdq_pack_weights_e3m2(R: torch.Tensor, wq6: torch.Tensor, w_scales: torch.T
     fn = "svdq_pack_weights_e3m2"
     K, N = R.shape
     a = _Args(fn)
-    args = (a(R, 4 * K * N, "R"), K, N, a(wq6, _e3m2_bytes(N, K), "wq6"),
-            a(w_scales, 2 * (K // 64) * N, "w_scales"))
+    args = (a(R, 4 * K * N, "R", _F32), K, N, a(wq6, _e3m2_bytes(N, K), "wq6", _U8),
+            a(w_scales, 2 * (K // 64) * N, "w_scales", _F16))
     _check(fn, load().svdq_pack_weights_e3m2(*args, a.stream(stream)))
 
 
@@ -260,8 +270,9 @@ def kv_int8_quant(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, zero: t
     fn = "kv_int8_quant"
     tokens, channels = _kv_shape(x)
     a = _Args(fn)
-    args = (a(x, 2 * tokens * channels, "x"), tokens, channels, a(q, tokens * channels, "q"),
-            a(scale, 4 * channels, "scale"), a(zero, channels, "zero"),
+    args = (a(x, 2 * tokens * channels, "x", _BF16), tokens, channels,
+            a(q, tokens * channels, "q", _U8), a(scale, 4 * channels, "scale", _F32),
+            a(zero, channels, "zero", _U8),
             a(workspace, kv_int8_workspace_bytes(tokens, channels) if tokens else 0, "workspace"))
     _check(fn, load().kv_int8_quant(*args, a.stream(stream)))
 
@@ -272,8 +283,9 @@ def kv_int8_dequant(q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
     fn = "kv_int8_dequant"
     tokens, channels = _kv_shape(q)
     a = _Args(fn)
-    args = (a(q, tokens * channels, "q"), a(scale, 4 * channels, "scale"),
-            a(zero, channels, "zero"), tokens, channels, a(x_out, 2 * tokens * channels, "x_out"))
+    args = (a(q, tokens * channels, "q", _U8), a(scale, 4 * channels, "scale", _F32),
+            a(zero, channels, "zero", _U8), tokens, channels,
+            a(x_out, 2 * tokens * channels, "x_out", _BF16))
     _check(fn, load().kv_int8_dequant(*args, a.stream(stream)))
 
 
@@ -321,8 +333,9 @@ def kv_int8_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scale: torch.Ten
     C = heads * dim
     ws = kv_int8_attention_workspace_bytes(nq, tokens, heads, dim) if nq and tokens else 0
     a = _Args(fn)
-    args = (a(q, 2 * nq * C, "q"), a(k_codes, tokens * C, "k_codes"), a(k_scale, 4 * C, "k_scale"),
-            a(k_zero, C, "k_zero"), a(v_codes, tokens * C, "v_codes"),
-            a(v_scale, 4 * C, "v_scale"), a(v_zero, C, "v_zero"), nq, tokens, heads, dim,
-            float(sm_scale), a(out, 2 * nq * C, "out"), a(workspace, ws, "workspace"))
+    args = (a(q, 2 * nq * C, "q", _BF16), a(k_codes, tokens * C, "k_codes", _U8),
+            a(k_scale, 4 * C, "k_scale", _F32), a(k_zero, C, "k_zero", _U8),
+            a(v_codes, tokens * C, "v_codes", _U8), a(v_scale, 4 * C, "v_scale", _F32),
+            a(v_zero, C, "v_zero", _U8), nq, tokens, heads, dim, float(sm_scale),
+            a(out, 2 * nq * C, "out", _BF16), a(workspace, ws, "workspace"))
     _check(fn, load().kv_int8_attention(*args, a.stream(stream)))

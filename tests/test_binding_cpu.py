@@ -1,6 +1,7 @@
-"""The binding's buffer checks: every tensor a call reads or writes must hold the bytes that the
-layouts in include/svdq.h give for the call's sizes, and a call with one buffer an element
-short raises ValueError naming it before anything reaches the library.
+"""The binding's buffer checks: every tensor a call reads or writes must have the dtype and
+hold the bytes that the layouts in include/svdq.h give for the call's sizes, and a call with
+one buffer an element short, or of another dtype, raises ValueError naming it before anything
+reaches the library.
 
 The stand-ins below carry a shape, a dtype and a byte size and claim to be device tensors;
 their pointers are never dereferenced, because every call here stops in the checks."""
@@ -15,9 +16,9 @@ from bit_post_quantized_amd import binding as B
 class Dev:
     """A stand-in for a contiguous device tensor of the given shape and dtype."""
 
-    def __init__(self, shape, dtype, short=False, device="cuda:0"):
+    def __init__(self, shape, dtype, short=False, device="cuda:0", as_dtype=None):
         self.shape = torch.Size(shape)
-        self.dtype = dtype
+        self.dtype = as_dtype or dtype
         self._n = math.prod(shape) - (1 if short else 0)
         self.device = torch.device(device)
         self.is_cuda = True
@@ -95,8 +96,15 @@ def _cases():
     ]
 
 
-def _args(order, tensors, scalars, short=None):
-    return [scalars[n] if n in scalars else Dev(*tensors[n], short=(n == short)) for n in order]
+def _args(order, tensors, scalars, short=None, retype=None):
+    return [scalars[n] if n in scalars else
+            Dev(*tensors[n], short=(n == short), as_dtype=_OTHER[tensors[n][1]] if n == retype
+                else None)
+            for n in order]
+
+
+# A different dtype of the same width, so that only the dtype check can catch it.
+_OTHER = {bf16: f16, f16: bf16, f32: i32, i32: f32, u8: i8, i8: u8}
 
 
 def _call(fn, order, tensors, scalars, short=None):
@@ -110,6 +118,19 @@ def test_each_short_buffer_is_rejected_by_name(case):
         with pytest.raises(ValueError, match="holds .* bytes") as e:
             _call(fn, order, tensors, scalars, short=name)
         assert f"{fn.__name__}: {name} holds" in str(e.value), (name, e.value)
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: c[0].__name__)
+def test_each_wrong_dtype_is_rejected_by_name(case):
+    fn, order, tensors, scalars = case
+    for name in tensors:
+        if name == "workspace":
+            continue  # raw bytes: any dtype
+        with pytest.raises(ValueError) as e:
+            fn(*_args(order, tensors, scalars, retype=name))
+        want = ("Y must be bfloat16 or float32" if name == "Y"
+                else f"{name} must be {tensors[name][1]}")
+        assert f"{fn.__name__}: {want}" in str(e.value), (name, e.value)
 
 
 def test_other_device_and_host_tensors_are_rejected():
