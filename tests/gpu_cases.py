@@ -23,6 +23,11 @@ SMALL = {
 FULL = {"c2": (2, None, None, None), "c3": (3, None, None, None), "c4": (4, None, None, None)}
 
 
+def with_bias(cases):
+    """(name, bias) pairs for the output tests: bias at the small shapes, none at full size."""
+    return [(n, b) for n in cases for b in (False, True) if not (b and n in FULL)]
+
+
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 

@@ -15,7 +15,7 @@ from oracle import svdquant as osq
 from oracle.numerics import bf16_to_bits, round_bf16
 from synthetic import make_linear
 from tests.gpu_cases import (FULL, SMALL, dev, dev_bf16, device_weights, host_u16, kv_case,
-                             linear_case, max_abs_rel, oracle_act)
+                             linear_case, max_abs_rel, oracle_act, with_bias)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -104,11 +104,8 @@ def _rows_for(M, full):
                                      rng.choice(M, 32, replace=False)]))
 
 
-@pytest.mark.parametrize("bias", [False, True])
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name,bias", with_bias(CASES))
 def test_gemm_output_within_tolerance(gpu_lib, name, bias):
-    if bias and name in FULL:
-        pytest.skip("bias is covered at the small shapes")
     case = _case(name, bias)
     d, pw, packed, r = case
     M, K = d["X"].shape

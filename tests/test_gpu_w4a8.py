@@ -7,7 +7,8 @@ import torch
 
 from bit_post_quantized_amd import binding as B
 from oracle import svdquant as osq
-from tests.gpu_cases import FULL, SMALL, dev_bf16, device_weights, host_u16, linear_case, max_abs_rel
+from tests.gpu_cases import (FULL, SMALL, dev_bf16, device_weights, host_u16, linear_case,
+                             max_abs_rel, with_bias)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -46,11 +47,8 @@ def test_act_a8_codes_scales_and_lowrank(gpu_lib, name):
     assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
 
 
-@pytest.mark.parametrize("bias", [False, True])
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name,bias", with_bias(CASES))
 def test_w4a8_gemm_output_within_tolerance(gpu_lib, name, bias):
-    if bias and name in FULL:
-        pytest.skip("bias is covered at the small shapes")
     case = _case(name, bias)
     d, pw, packed, r = case
     M = d["X"].shape[0]
