@@ -154,6 +154,7 @@ def test_kv_attention_validation(lib):
     assert a(*p7, 0, 16, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EINVAL     # nq
     assert a(*p7, 1, 0, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EINVAL      # no tokens
     assert a(*p7, 1, 16, 4, 64, 0.1, FAKE, None, None) == binding.SVDQ_EINVAL     # workspace
+    assert a(*p7, 1, 1048577, 1, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_ESHAPE  # 4097 chunks
     assert a(ODD, *p7[1:], 1, 16, 4, 64, 0.1, FAKE, FAKE, None) == binding.SVDQ_EALIGN
     assert a(*p7, 1, 16, 4, 64, float("nan"), FAKE, FAKE, None) == binding.SVDQ_EINVAL
     assert b"sm_scale" in lib.svdq_last_error()

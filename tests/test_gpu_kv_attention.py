@@ -46,6 +46,8 @@ def _run(q_bits, cache, heads, dim, sm_scale):
     (1000, 8, 64, 3),
     (257, 2, 128, 1),       # a one-token tail chunk
     (10240, 32, 128, 1),    # the cache shape of the KV workload
+    (70000, 2, 64, 1),      # 274 chunks: more chunks than combine threads
+    (1048576, 1, 64, 1),    # 4096 chunks, the most one call takes
 ])
 def test_attention_matches_the_oracle(gpu_lib, tokens, heads, dim, nq):
     cache = _cache(tokens, heads, dim)
