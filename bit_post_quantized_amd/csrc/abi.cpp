@@ -38,6 +38,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr long long kMaxElems = 1LL << 40;  // keeps every byte offset far inside size_t
 constexpr int kMaxRank = 128;
+// The KV dequantization's grid holds the tokens in its y dimension, at most 65535 blocks of 32.
+constexpr int kKvMaxTokens = 65535 * 32;
 
 int check_k(int K) {
   if (K <= 0) return fail(SVDQ_EINVAL, "K must be positive (got %d)", K);
@@ -230,7 +232,8 @@ static int check_kv(int tokens, int channels) {
   if (channels <= 0) return fail(SVDQ_EINVAL, "channels must be positive (got %d)", channels);
   if (channels % 8 != 0) return fail(SVDQ_ESHAPE, "channels must be a multiple of 8 (got %d)", channels);
   if ((long long)tokens * channels > kMaxElems) return fail(SVDQ_ESHAPE, "tensor too large");
-  if ((tokens + 63) / 64 > 65535) return fail(SVDQ_ESHAPE, "too many tokens for one launch");
+  if (tokens > kKvMaxTokens)
+    return fail(SVDQ_ESHAPE, "tokens must be <= %d (got %d)", kKvMaxTokens, tokens);
   return SVDQ_OK;
 }
 

@@ -200,7 +200,7 @@ size_t kv_int8_workspace_bytes(int tokens, int channels);
  *   q          uint8 [tokens, channels]                   16B
  *   scale      fp32 [channels]    16B;   zero  uint8 [channels]    16B
  *   workspace  device scratch of kv_int8_workspace_bytes(tokens, channels) bytes    16B
- *   tokens >= 0, channels >= 8, channels % 8 == 0.
+ *   0 <= tokens <= 2097120 (65535 * 32), channels >= 8, channels % 8 == 0.
  */
 int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float* scale,
                   uint8_t* zero, void* workspace, void* stream);
@@ -209,7 +209,7 @@ int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float
  * kv_int8_dequant — x' = bf16(fl32((q - z) * s)) per element (round to nearest even).
  *   q      uint8 [tokens, channels]   16B;   x_out  bf16 [tokens, channels]   16B
  *   scale, zero as written by kv_int8_quant   16B
- *   tokens >= 0, channels >= 8, channels % 8 == 0.
+ *   0 <= tokens <= 2097120 (65535 * 32), channels >= 8, channels % 8 == 0.
  */
 int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
                     int channels, uint16_t* x_out, void* stream);

@@ -142,6 +142,10 @@ def test_kv_validation(lib):
     d = lib.kv_int8_dequant
     assert d(FAKE, FAKE, FAKE, 16, 0, FAKE, None) == binding.SVDQ_EINVAL
     assert d(FAKE, FAKE, FAKE, 16, 16, ODD, None) == binding.SVDQ_EALIGN
+    # the dequantization's grid: at most 65535 blocks of 32 tokens, for both calls
+    assert q(FAKE, 65535 * 32 + 1, 8, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
+    assert d(FAKE, FAKE, FAKE, 65535 * 32 + 1, 8, FAKE, None) == binding.SVDQ_ESHAPE
+    assert b"2097120" in lib.svdq_last_error()
 
 
 def test_kv_attention_validation(lib):

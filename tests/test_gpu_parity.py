@@ -276,9 +276,11 @@ def _gpu_kv(x_bits):
 # (2000, 16, 128) is a single pass over 16 slabs, (1000, 8, 64) over 4 and (300, 3, 128) over 3;
 # 1000 and 100 tokens end in a partial 64-token range chunk of the three-pass schedule; 12800
 # tokens (three passes) fill 200 chunks; (1, 2, 8) is a single token of 16 channels; (5, 2, 128)
-# is a single pass in which some token parts are empty
+# is a single pass in which some token parts are empty; 2097120 tokens is the most one call
+# takes (65535 dequantization blocks of 32 tokens; three passes over 32768 range chunks)
 @pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64),
-                                   (2000, 16, 128), (5, 2, 128), (300, 3, 128), (12800, 32, 128)])
+                                   (2000, 16, 128), (5, 2, 128), (300, 3, 128), (12800, 32, 128),
+                                   (2097120, 1, 8)])
 def test_kv_quant_dequant_bitexact(gpu_lib, shape):
     for name, (x, ref) in kv_case(*shape).items():
         q, s, z, xo = _gpu_kv(x)
