@@ -208,10 +208,10 @@ def main():
         b = i % ROTATE
         a = acts[b]
         calls = [
-            ("act", lambda: B.svdq_quantize_act_e3m2(X[b], pw.inv_lambda, pw.L1t, RANK, a.xq,
+            ("act", lambda: B.svdq_quantize_act_e3m2(X[b], pw.inv_lambda, pw.L1p, RANK, a.xq,
                                                      a.x_scales, a.T, stream)),
             ("gemm", lambda: B.svdq_w4a4_gemm_e3m2(a.xq, a.x_scales, a.T, pw.wq, pw.w_scales,
-                                                   pw.L2t, None, RANK, Y[b], stream)),
+                                                   pw.L2, None, RANK, Y[b], stream)),
         ]
         for t in range(2):
             calls.append(("kv_quant", lambda t=t: B.kv_int8_quant(kvs[b][t], q[b][t], sc[b][t],
@@ -260,7 +260,7 @@ def main():
     # ---- the INT8-unit route on the same batch, outside the timed region
     B.svdq_pack_weights(pw.R32, wq4, ws4)
     xq4 = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
-    xs4 = torch.empty(K // 64, M, dtype=torch.float16, device=dev)
+    xs4 = torch.empty(M, K // 64, dtype=torch.float16, device=dev)
     T4 = torch.empty(M, RANK, dtype=torch.float32, device=dev)
     xq8 = torch.empty(M, K, dtype=torch.int8, device=dev)   # W4A8 variant: 8-bit activations
 
@@ -278,15 +278,15 @@ def main():
         return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     int8_ms = {
-        "act": time10(lambda: B.svdq_quantize_act(X[0], pw.inv_lambda, pw.L1t, RANK, xq4, xs4,
+        "act": time10(lambda: B.svdq_quantize_act(X[0], pw.inv_lambda, pw.L1p, RANK, xq4, xs4,
                                                   T4, stream)),
-        "gemm": time10(lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
+        "gemm": time10(lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2, None, RANK, Y[0],
                                                 stream)),
     }
     w4a8_ms = {
-        "act": time10(lambda: B.svdq_quantize_act_a8(X[0], pw.inv_lambda, pw.L1t, RANK, xq8, xs4,
+        "act": time10(lambda: B.svdq_quantize_act_a8(X[0], pw.inv_lambda, pw.L1p, RANK, xq8, xs4,
                                                      T4, stream)),
-        "gemm": time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2t, None, RANK, Y[0],
+        "gemm": time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2, None, RANK, Y[0],
                                                 stream)),
     }
     # LoRA: a seeded rank-16 adapter joined to the 16-bit branch (rank 32 + 16 = 48), FP6 route,
@@ -296,10 +296,10 @@ def main():
                             torch.randn(LORA_RANK, N, generator=gl, dtype=torch.float64) * 0.02)
     al = layer.alloc_act(M, K, pwl.rank, dev, e3m2=True)
     lora_ms = {
-        "act": time10(lambda: B.svdq_quantize_act_e3m2(X[0], pwl.inv_lambda, pwl.L1t, pwl.rank,
+        "act": time10(lambda: B.svdq_quantize_act_e3m2(X[0], pwl.inv_lambda, pwl.L1p, pwl.rank,
                                                        al.xq, al.x_scales, al.T, stream)),
         "gemm": time10(lambda: B.svdq_w4a4_gemm_e3m2(al.xq, al.x_scales, al.T, pwl.wq,
-                                                     pwl.w_scales, pwl.L2t, None, pwl.rank, Y[0],
+                                                     pwl.w_scales, pwl.L2, None, pwl.rank, Y[0],
                                                      stream)),
     }
     # decode attention over the INT8 cache of batch 0 (one query per head): reads the codes

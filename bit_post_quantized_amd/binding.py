@@ -28,6 +28,7 @@ _SIGNATURES = {
     "svdq_status_str": ([_I], ctypes.c_char_p),
     "svdq_last_error": ([], ctypes.c_char_p),
     "svdq_pack_weights": ([_P, _I, _I, _P, _P, _P], _I),
+    "svdq_pack_lowrank": ([_P, _I, _I, _P, _P], _I),
     "svdq_quantize_act": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "svdq_w4a4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "svdq_w4a4_partials": ([_P, _P, _I, _I, _I, _P, _P], _I),
@@ -89,13 +90,16 @@ class _Args:
         self.device: Optional[torch.device] = None
 
     def __call__(self, t: Optional[torch.Tensor], need: int, name: str,
-                 dtype: Optional[torch.dtype] = None):
+                 dtype: Optional[torch.dtype] = None, shape: Optional[tuple] = None):
         if t is None:
             return None
         if not t.is_cuda:
             raise ValueError(f"{self.fn}: {name} must be a device tensor")
         if dtype is not None and t.dtype != dtype:
             raise ValueError(f"{self.fn}: {name} must be {dtype} (got {t.dtype})")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.fn}: {name} must have shape {tuple(shape)} "
+                             f"(got {tuple(t.shape)})")
         if not t.is_contiguous():
             raise ValueError(f"{self.fn}: {name} must be contiguous")
         if self.device is None:
@@ -148,23 +152,33 @@ def svdq_pack_weights(R: torch.Tensor, wq: torch.Tensor, w_scales: torch.Tensor,
     _check(fn, load().svdq_pack_weights(*args, a.stream(stream)))
 
 
-def svdq_quantize_act(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[torch.Tensor],
+def svdq_pack_lowrank(L1: torch.Tensor, L1p: torch.Tensor, stream=None) -> None:
+    """L1 bf16 [K, r] -> L1p bf16 [r, K], the activation pass's layout of the factor."""
+    fn = "svdq_pack_lowrank"
+    K, r = L1.shape
+    a = _Args(fn)
+    args = (a(L1, 2 * K * r, "L1", _BF16, (K, r)), K, r, a(L1p, 2 * r * K, "L1p", _BF16, (r, K)))
+    _check(fn, load().svdq_pack_lowrank(*args, a.stream(stream)))
+
+
+def svdq_quantize_act(X: torch.Tensor, inv_lambda: torch.Tensor, L1p: Optional[torch.Tensor],
                       r: int, xq: torch.Tensor, x_scales: torch.Tensor,
                       T: Optional[torch.Tensor], stream=None) -> None:
-    """X bf16 [M, K], inv_lambda fp32 [K], L1 bf16 [r, K] (K-contiguous) ->
-    xq uint8 [M, K/2], x_scales fp16 [K/64, M], T fp32 [M, r]."""
-    _quantize_act("svdq_quantize_act", X, inv_lambda, L1, r, xq, "xq",
+    """X bf16 [M, K], inv_lambda fp32 [K], L1p bf16 [r, K] (from svdq_pack_lowrank) ->
+    xq uint8 [M, K/2], x_scales fp16 [M, K/64], T fp32 [M, r]."""
+    _quantize_act("svdq_quantize_act", X, inv_lambda, L1p, r, xq, "xq",
                   X.shape[0] * (X.shape[1] // 2), x_scales, T, stream)
 
 
-def _quantize_act(fn, X, inv_lambda, L1, r, codes, code_name, code_bytes, x_scales, T,
+def _quantize_act(fn, X, inv_lambda, L1p, r, codes, code_name, code_bytes, x_scales, T,
                   stream) -> None:
     M, K = X.shape
     a = _Args(fn)
-    args = (a(X, 2 * M * K, "X", _BF16), a(inv_lambda, 4 * K, "inv_lambda", _F32),
-            a(L1, 2 * r * K, "L1", _BF16), M, K, r,
+    args = (a(X, 2 * M * K, "X", _BF16, (M, K)), a(inv_lambda, 4 * K, "inv_lambda", _F32, (K,)),
+            a(L1p, 2 * r * K, "L1p", _BF16, (r, K)), M, K, r,
             a(codes, code_bytes, code_name, _I8 if code_name == "xq8" else _U8),
-            a(x_scales, 2 * (K // 64) * M, "x_scales", _F16), a(T, 4 * M * r, "T", _F32))
+            a(x_scales, 2 * (K // 64) * M, "x_scales", _F16, (M, K // 64)),
+            a(T, 4 * M * r, "T", _F32, (M, r)))
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
@@ -174,17 +188,18 @@ def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L
     a = _Args(fn)
     G = K // 64
     args = (a(xq, x_bytes, x_name, _I8 if x_name == "xq8" else _U8),
-            a(x_scales, 2 * G * M, "x_scales", _F16), a(T, 4 * M * r, "T", _F32),
-            a(wq, w_bytes, w_name, _U8), a(w_scales, 2 * G * N, "w_scales", _F16),
-            a(L2, 2 * r * N, "L2", _BF16), a(bias, 2 * N, "bias", _BF16),
-            M, N, K, r, a(Y, Y.element_size() * M * N, "Y"), out)
+            a(x_scales, 2 * G * M, "x_scales", _F16, (M, G)), a(T, 4 * M * r, "T", _F32, (M, r)),
+            a(wq, w_bytes, w_name, _U8), a(w_scales, 2 * G * N, "w_scales", _F16, (G, N)),
+            a(L2, 2 * r * N, "L2", _BF16, (r, N)), a(bias, 2 * N, "bias", _BF16, (N,)),
+            M, N, K, r, a(Y, Y.element_size() * M * N, "Y", None, (M, N)), out)
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
 def _partials(fn, xq, x_name, x_bytes, wq, w_name, w_bytes, M, N, K, P, stream) -> None:
     a = _Args(fn)
     args = (a(xq, x_bytes, x_name, _I8 if x_name == "xq8" else _U8),
-            a(wq, w_bytes, w_name, _U8), M, N, K, a(P, 4 * (K // 64) * M * N, "P", _I32))
+            a(wq, w_bytes, w_name, _U8), M, N, K,
+            a(P, 4 * (K // 64) * M * N, "P", _I32, (K // 64, M, N)))
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
@@ -224,11 +239,11 @@ def svdq_pack_weights_e3m2(R: torch.Tensor, wq6: torch.Tensor, w_scales: torch.T
 
 
 def svdq_quantize_act_e3m2(X: torch.Tensor, inv_lambda: torch.Tensor,
-                           L1: Optional[torch.Tensor], r: int, xq6: torch.Tensor,
+                           L1p: Optional[torch.Tensor], r: int, xq6: torch.Tensor,
                            x_scales: torch.Tensor, T: Optional[torch.Tensor],
                            stream=None) -> None:
     """As svdq_quantize_act with the codes written to xq6, the tiled BF6 container of M rows."""
-    _quantize_act("svdq_quantize_act_e3m2", X, inv_lambda, L1, r, xq6, "xq6",
+    _quantize_act("svdq_quantize_act_e3m2", X, inv_lambda, L1p, r, xq6, "xq6",
                   _e3m2_bytes(X.shape[0], X.shape[1]), x_scales, T, stream)
 
 
@@ -236,10 +251,10 @@ def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[t
                         wq6: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
                         bias: Optional[torch.Tensor], r: int, Y: torch.Tensor,
                         stream=None) -> None:
-    """As svdq_w4a4_gemm, reading the BF6 containers (M, N, K from x_scales [K/64, M] and
-    w_scales [K/64, N])."""
-    G, M = x_scales.shape
-    N = w_scales.shape[1]
+    """As svdq_w4a4_gemm, reading the BF6 containers (M, N from Y [M, N], K from
+    w_scales [K/64, N]; every other tensor's shape is checked against them)."""
+    M, N = Y.shape
+    G = w_scales.shape[0]
     K = 64 * G
     _gemm("svdq_w4a4_gemm_e3m2", xq6, "xq6", _e3m2_bytes(M, K), x_scales, T, wq6, "wq6",
           _e3m2_bytes(N, K), w_scales, L2, bias, M, N, K, r, Y, stream)
@@ -289,12 +304,12 @@ def kv_int8_dequant(q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,
     _check(fn, load().kv_int8_dequant(*args, a.stream(stream)))
 
 
-def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1: Optional[torch.Tensor],
+def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1p: Optional[torch.Tensor],
                          r: int, xq8: torch.Tensor, x_scales: torch.Tensor,
                          T: Optional[torch.Tensor], stream=None) -> None:
-    """W4A8 activation pass: X bf16 [M, K] -> xq8 int8 [M, K], x_scales fp16 [K/64, M],
+    """W4A8 activation pass: X bf16 [M, K] -> xq8 int8 [M, K], x_scales fp16 [M, K/64],
     T fp32 [M, r]."""
-    _quantize_act("svdq_quantize_act_a8", X, inv_lambda, L1, r, xq8, "xq8",
+    _quantize_act("svdq_quantize_act_a8", X, inv_lambda, L1p, r, xq8, "xq8",
                   X.shape[0] * X.shape[1], x_scales, T, stream)
 
 

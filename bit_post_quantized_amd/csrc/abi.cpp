@@ -95,6 +95,16 @@ int svdq_pack_weights_e3m2(const float* R, int K, int N, uint8_t* wq6, uint16_t*
   return pack_weights(R, K, N, wq6, w_scales, stream, 1, "svdq_pack_weights_e3m2");
 }
 
+int svdq_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p, void* stream) {
+  if (int s = check_k(K)) return s;
+  if (int s = check_rank(r)) return s;
+  if (r == 0) return fail(SVDQ_ESHAPE, "r must be positive for the factor relayout");
+  if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535");
+  if (!L1 || !L1p) return fail(SVDQ_EINVAL, "NULL pointer");
+  return hip_status(svdq::launch_pack_lowrank(L1, K, r, L1p, (hipStream_t)stream),
+                    "svdq_pack_lowrank");
+}
+
 static int quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
                         int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream,
                         int codes, const char* name) {
@@ -138,6 +148,8 @@ static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K)
   if ((long long)M * N > kMaxElems || (long long)M * K > kMaxElems || (long long)N * K > kMaxElems)
     return fail(SVDQ_ESHAPE, "problem too large");
   if ((M + 127) / 128 > 65535) return fail(SVDQ_ESHAPE, "M too large for one launch");
+  // row offsets inside an output tile (< 256 N) are 32-bit in the kernels
+  if (N > (1 << 24)) return fail(SVDQ_ESHAPE, "N must be <= 2^24 (got %d)", N);
   if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535 (got K = %d)", K);
   if (!xq || !wq) return fail(SVDQ_EINVAL, "NULL pointer");
   if (!aligned16(xq) || !aligned16(wq)) return fail(SVDQ_EALIGN, "xq and wq must be 16-byte aligned");

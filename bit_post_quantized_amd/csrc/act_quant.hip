@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
           if constexpr (I8)  // c + 128 xor 128 is the two's complement byte of c
             *reinterpret_cast<v4u*>(xq + (size_t)row * K + (size_t)g * kGroup + 16 * q) =
                 v4u{bq[0], bq[1], bq[2], bq[3]} ^ 0x80808080u;
-          if (q == 0) x_scales[(size_t)g * M + row] = sb;
+          if (q == 0) x_scales[(size_t)row * G + g] = sb;  // [M, G]
         }
       }
 

@@ -414,10 +414,16 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
   for (int k = 0; k < R; ++k) asm volatile("" : "+v"(v[k]));
 
   // ---- publish this part's range, then wait (bounded) for the other parts
+  // Publication order: waves 0 and 1 store the part's range (channels 0..63 and 64..127); each
+  // of them releases its own stores at agent scope before the barrier, so both halves are
+  // visible device-wide before any wave passes the barrier, and so before thread 0's
+  // release store of the tag that the other parts acquire.  (The tag's release alone orders
+  // only the stores of the wave that issues it.)
   float* mine = parts + ((size_t)slab * kFusedParts + part) * 2 * kFusedCh;
-  if (tid < kFusedCh) {
+  if (tid < kFusedCh) {  // whole waves 0 and 1
     mine[tid] = plo;
     mine[kFusedCh + tid] = phi;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   }
   __syncthreads();
   if (tid < 64) {  // wave 0: lane p < kFusedParts watches part p's tag

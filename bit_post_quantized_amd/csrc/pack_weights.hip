@@ -80,4 +80,31 @@ hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16
   return hipGetLastError();
 }
 
+// Low-rank factor relayout (offline weight preparation, like the residual packing above): the
+// [K, r] factor L1 of the 16-bit branch (SVDQ "technical principles") becomes [r, K], each
+// rank's K values contiguous, the layout the activation pass reads (one row's 64-value group
+// slice of a rank per 16-byte pair).  A plain transpose through LDS in 64 x 64 tiles (bf16
+// values copied, no arithmetic).
+__global__ __launch_bounds__(256) void pack_lowrank_kernel(const uint16_t* __restrict__ L1, int K,
+                                                           int r, uint16_t* __restrict__ L1p) {
+  __shared__ uint16_t tile[64][65];
+  const int k0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, jj = i % 64;  // coalesced over the rank index of a row of L1
+    if (k0 + kk < K && j0 + jj < r) tile[kk][jj] = L1[(size_t)(k0 + kk) * r + j0 + jj];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int jj = i / 64, kk = i % 64;  // coalesced over k of a row of L1p
+    if (k0 + kk < K && j0 + jj < r) L1p[(size_t)(j0 + jj) * K + k0 + kk] = tile[kk][jj];
+  }
+}
+
+hipError_t launch_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p,
+                               hipStream_t stream) {
+  const dim3 grid((K + 63) / 64, (r + 63) / 64);
+  hipLaunchKernelGGL(pack_lowrank_kernel, grid, dim3(256), 0, stream, L1, K, r, L1p);
+  return hipGetLastError();
+}
+
 }  // namespace svdq

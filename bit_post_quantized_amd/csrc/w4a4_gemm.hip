@@ -4,7 +4,7 @@
 // low-bit kernel so it costs no extra pass over the activations.  W4A8 2.2 / 4.2: 4-bit
 // weights are widened to 8 bits and fed to the INT8 units.  Per 64-group g of K the int32
 // partial P[g] = qx[:, g] . qw[g, :] is exact, and
-//     Y = sum_g diag(s_x[g]) P[g] diag(s_w[g]) + bf16(T) L2 + bias.
+//     Y = sum_g diag(s_x[:, g]) P[g] diag(s_w[g]) + bf16(T) L2 + bias.
 //
 // gfx950 mapping (one workgroup = 4 waves = a 128 x 128 tile of Y; wave (wm, wn) owns the
 // 64 x 64 sub-tile made of 4 x 4 tiles of 16 x 16):
@@ -106,9 +106,9 @@ void w4a4_gemm_kernel(
     const int e = tid + u * NT;
     const bool is_a = e < TM;
     s_src[u] = PARTIALS ? nullptr
-               : is_a ? x_scales + min(m_tile + e, M - 1)
-                      : w_scales + min(n_tile + e - TM, N - 1);
-    s_stride[u] = is_a ? (size_t)M : (size_t)N;
+               : is_a ? x_scales + (size_t)min(m_tile + e, M - 1) * G  // s_x [M, G]
+                      : w_scales + min(n_tile + e - TM, N - 1);       // s_w [G, N]
+    s_stride[u] = is_a ? (size_t)1 : (size_t)N;
   }
 
   auto stage_ptr = [&](int buf) { return lds + buf * kStageBytes; };
@@ -258,9 +258,15 @@ void w4a4_gemm_kernel(
       v8bf Bt[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        v4u b = v4u{0u, 0u, 0u, 0u};
-        if (kv) b = *reinterpret_cast<const v4u*>(L2 + (size_t)min(col0 + 16 * j + rl, No - 1) * r + kk);
-        Bt[j] = __builtin_bit_cast(v8bf, b);
+        // L2 [r, N]: this lane's column, ranks kk .. kk + 7
+        uint32_t b[4] = {0u, 0u, 0u, 0u};
+        if (kv) {
+          const uint16_t* lp = L2 + (size_t)kk * No + min(col0 + 16 * j + rl, No - 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            b[q] = (uint32_t)lp[(size_t)(2 * q) * No] | ((uint32_t)lp[(size_t)(2 * q + 1) * No] << 16);
+        }
+        Bt[j] = __builtin_bit_cast(v8bf, v4u{b[0], b[1], b[2], b[3]});
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {

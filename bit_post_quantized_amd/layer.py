@@ -8,6 +8,8 @@ it is the offline preparation a toolbox performs once per checkpoint, not part o
 per-token path.
 
 Forward (device): ``svdq_quantize_act`` then ``svdq_w4a4_gemm``, two launches on one stream.
+The factor L1 [K, r] is relaid out once to the activation pass's [r, K] by
+``svdq_pack_lowrank``; L2 [r, N] is read by the GEMM as it is.
 With ``e3m2=True`` the codes travel as BF6 (E3M2) values and the ``*_e3m2`` entry points run
 the GEMM on the FP6 matrix units (same codes, scales and result; the faster path on gfx950).
 """
@@ -28,8 +30,8 @@ class PackedWeights:
     N: int
     rank: int
     inv_lambda: torch.Tensor  # fp32 [K]
-    L1t: torch.Tensor         # bf16 [r, K]  (the [K, r] factor stored K-contiguous)
-    L2t: torch.Tensor         # bf16 [N, r]  (the [r, N] factor stored r-contiguous)
+    L1p: torch.Tensor         # bf16 [r, K]  (the [K, r] factor, from svdq_pack_lowrank)
+    L2: torch.Tensor          # bf16 [r, N]
     wq: torch.Tensor          # uint8 [N, K/2] (nibbles) or the tiled BF6 container of N rows
     w_scales: torch.Tensor    # fp16 [K/64, N]
     bias: Optional[torch.Tensor] = None  # bf16 [N]
@@ -49,10 +51,23 @@ def _bf16_rn(x: torch.Tensor) -> torch.Tensor:
     return (t.view(torch.int32) | inexact).view(torch.float32).to(torch.bfloat16)
 
 
-def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
-                    bias: Optional[torch.Tensor] = None, device="cuda",
-                    e3m2: bool = False, keep_residual: bool = False) -> PackedWeights:
-    """W bf16 [K, N] (Y = X W), X_calib bf16 [M, K] calibration activations."""
+@dataclass
+class HostWeights:
+    """The offline host half of the weight conversion (all CPU tensors)."""
+    lam: torch.Tensor         # fp32 [K] smoothing factors
+    inv_lambda: torch.Tensor  # fp32 [K] = fl32(1 / lam)
+    L1b: torch.Tensor         # bf16 [K, r]
+    L2b: torch.Tensor         # bf16 [r, N]
+    R32: torch.Tensor         # fp32 [K, N] residual W^ - L1b L2b
+
+
+def prepare_host(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int) -> HostWeights:
+    """Smoothing factors from the calibration activations, the rank-r split of the smoothed
+    weight kept in bf16, and the fp32 residual (SVDQ "technical principles"; FLUX4 2.2).
+
+    W bf16 [K, N] (Y = X W), X_calib bf16 [M, K].  lam_k = max|X_k|^alpha / max|W_k|^(1-alpha)
+    (1 where either is 0), W^ = diag(lam32) W in fp64, L1 = U_r S_r and L2 = V_r^T rounded once
+    to bf16, R = W^ - L1b L2b in fp64 stored as fp32."""
     K, N = W.shape
     Wd = W.detach().to("cpu", torch.float64)
     Xd = X_calib.detach().to("cpu", torch.float64)
@@ -73,7 +88,18 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
         L1b = torch.zeros(K, 0, dtype=torch.bfloat16)
         L2b = torch.zeros(0, N, dtype=torch.bfloat16)
         R = W_hat
-    R32 = R.to(torch.float32).to(device).contiguous()
+    return HostWeights(lam=lam32, inv_lambda=inv32, L1b=L1b, L2b=L2b,
+                       R32=R.to(torch.float32).contiguous())
+
+
+def pack_device(hw: HostWeights, bias: Optional[torch.Tensor] = None, device="cuda",
+                e3m2: bool = False, keep_residual: bool = False) -> PackedWeights:
+    """The device half of the weight conversion: the residual's INT4 codes and scales
+    (``svdq_pack_weights``, or ``svdq_pack_weights_e3m2`` for the BF6 container) and the factor
+    relayout (``svdq_pack_lowrank``)."""
+    K, N = hw.R32.shape
+    rank = hw.L1b.shape[1]
+    R32 = hw.R32.to(device).contiguous()
     w_scales = torch.empty(K // 64, N, dtype=torch.float16, device=device)
     if e3m2:
         wq = torch.empty(binding.svdq_e3m2_bytes(N, K), dtype=torch.uint8, device=device)
@@ -82,11 +108,28 @@ def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: 
         wq = torch.empty(N, K // 2, dtype=torch.uint8, device=device)
         binding.svdq_pack_weights(R32, wq, w_scales)
     return PackedWeights(
-        K=K, N=N, rank=rank, inv_lambda=inv32.to(device),
-        L1t=L1b.t().contiguous().to(device), L2t=L2b.t().contiguous().to(device),
+        K=K, N=N, rank=rank, inv_lambda=hw.inv_lambda.to(device),
+        L1p=pack_lowrank(hw.L1b.to(device)), L2=hw.L2b.contiguous().to(device),
         wq=wq, w_scales=w_scales,
         bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2,
-        R32=R32 if keep_residual else None, lam=lam32)
+        R32=R32 if keep_residual else None, lam=hw.lam)
+
+
+def convert_weights(W: torch.Tensor, X_calib: torch.Tensor, alpha: float, rank: int,
+                    bias: Optional[torch.Tensor] = None, device="cuda",
+                    e3m2: bool = False, keep_residual: bool = False) -> PackedWeights:
+    """W bf16 [K, N] (Y = X W), X_calib bf16 [M, K] calibration activations: ``prepare_host``
+    then ``pack_device``."""
+    return pack_device(prepare_host(W, X_calib, alpha, rank), bias, device, e3m2, keep_residual)
+
+
+def pack_lowrank(L1: torch.Tensor) -> torch.Tensor:
+    """L1 bf16 [K, r] on the device -> L1p [r, K] (``svdq_pack_lowrank``); [0, K] for r = 0."""
+    K, r = L1.shape
+    L1p = torch.empty(r, K, dtype=torch.bfloat16, device=L1.device)
+    if r:
+        binding.svdq_pack_lowrank(L1.contiguous(), L1p)
+    return L1p
 
 
 def attach_lora(pw: PackedWeights, A: torch.Tensor, B: torch.Tensor,
@@ -107,12 +150,12 @@ def attach_lora(pw: PackedWeights, A: torch.Tensor, B: torch.Tensor,
     r2 = pw.rank + rl
     if r2 % 16 or r2 > 128:
         raise ValueError(f"combined rank {r2} must be a multiple of 16 and at most 128")
-    dev = pw.L1t.device
+    dev = pw.L1p.device
     A_hat = _bf16_rn(pw.lam.to("cpu", torch.float64)[:, None] * A.to("cpu", torch.float64))
     B_s = _bf16_rn(scale * B.to("cpu", torch.float64))
-    L1t = torch.cat([pw.L1t, A_hat.t().to(dev)], dim=0).contiguous()
-    L2t = torch.cat([pw.L2t, B_s.t().to(dev)], dim=1).contiguous()
-    return dataclasses.replace(pw, rank=r2, L1t=L1t, L2t=L2t)
+    L1p = torch.cat([pw.L1p, pack_lowrank(A_hat.to(dev))], dim=0).contiguous()
+    L2 = torch.cat([pw.L2, B_s.to(dev)], dim=0).contiguous()
+    return dataclasses.replace(pw, rank=r2, L1p=L1p, L2=L2)
 
 
 @dataclass
@@ -126,7 +169,7 @@ def alloc_act(M: int, K: int, rank: int, device="cuda", e3m2: bool = False) -> A
     return ActBuffers(
         xq=(torch.empty(binding.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device=device) if e3m2
             else torch.empty(M, K // 2, dtype=torch.uint8, device=device)),
-        x_scales=torch.empty(K // 64, M, dtype=torch.float16, device=device),
+        x_scales=torch.empty(M, K // 64, dtype=torch.float16, device=device),
         T=torch.empty(M, rank, dtype=torch.float32, device=device) if rank > 0 else None)
 
 
@@ -141,8 +184,8 @@ def forward(X: torch.Tensor, pw: PackedWeights, out: Optional[torch.Tensor] = No
         out = torch.empty(M, pw.N, dtype=out_dtype, device=X.device)
     quantize = binding.svdq_quantize_act_e3m2 if pw.e3m2 else binding.svdq_quantize_act
     gemm = binding.svdq_w4a4_gemm_e3m2 if pw.e3m2 else binding.svdq_w4a4_gemm
-    quantize(X, pw.inv_lambda, pw.L1t if pw.rank else None, pw.rank, act.xq, act.x_scales,
+    quantize(X, pw.inv_lambda, pw.L1p if pw.rank else None, pw.rank, act.xq, act.x_scales,
              act.T, stream)
-    gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales, pw.L2t if pw.rank else None,
+    gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales, pw.L2 if pw.rank else None,
          pw.bias, pw.rank, out, stream)
     return out

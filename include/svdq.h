@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 4
+#define SVDQ_ABI_VERSION 5
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -73,6 +73,16 @@ int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_sca
                       void* stream);
 
 /*
+ * svdq_pack_lowrank — relayout of the 16-bit branch's down-projection factor for the activation
+ * pass (offline weight preparation, like svdq_pack_weights; SVDQ "technical principles": the
+ * rank-r branch L1 L2 kept in 16 bits).  Values are copied, not rounded.
+ *   L1    bf16 [K, r] (row-major: element (k, j) at L1[k * r + j])
+ *   L1p   bf16 [r, K] (element (k, j) at L1p[j * K + k]: each rank's K values contiguous)
+ *   K % 64 == 0, K >= 64, 16 <= r <= 128, r % 16 == 0.
+ */
+int svdq_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p, void* stream);
+
+/*
  * svdq_quantize_act — one HBM pass over the activations: smoothing divide (a multiply by the
  * stored reciprocal inv_lambda), dynamic symmetric INT4 quantization per (token, 64-group)
  * (FLUX4 3.1 "dynamic activation quantization"; W4A8 3.1), and the low-rank down-projection
@@ -80,30 +90,30 @@ int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_sca
  *     X^ = fl32(X * inv_lambda);  s = fp16(fl32(amax / 7));  q = clamp(rne(fl32(X^ / s)), -8, 7)
  *   X           bf16 [M, K]                               16B
  *   inv_lambda  fp32 [K]                                  16B
- *   L1          bf16, the [K, r] factor stored K-contiguous: element (k, j) at L1[j*K + k]
- *               (16B); may be NULL when r == 0
+ *   L1p         bf16 [r, K], the factor L1 [K, r] as written by svdq_pack_lowrank (16B); may be
+ *               NULL when r == 0
  *   xq          uint8 [M, K/2], nibble order as wq        16B
- *   x_scales    fp16 [G, M]  (group-major: the scales of one group are contiguous over tokens)
+ *   x_scales    fp16 [M, K/64] (row-major: token m's G scales contiguous)
  *   T           fp32 [M, r]; may be NULL when r == 0
  *   M >= 0, K % 64 == 0, K >= 64, 0 <= r <= 128, r % 16 == 0.
  */
-int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
+int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1p, int M,
                       int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream);
 
 /*
  * svdq_w4a4_gemm — the W4A4 group GEMM with the low-rank branch and bias fused into its
  * epilogue (SVDQ "Nunchaku" kernel fusion; DCMP "SVDQuant" section):
- *     Y[m, n] = sum_g s_x[g, m] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
+ *     Y[m, n] = sum_g s_x[m, g] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
  *     P[g, m, n] = sum_{k in group g} qx[m, k] qw[n, k]   (exact int32).
  *   xq, x_scales, T   as written by svdq_quantize_act (T: 16B; may be NULL when r == 0)
  *   wq, w_scales      as written by svdq_pack_weights
- *   L2          bf16, the [r, N] factor stored r-contiguous: element (j, n) at L2[n*r + j]
- *               (16B); may be NULL when r == 0
+ *   L2          bf16 [r, N] (row-major: element (j, n) at L2[j * N + n]) (16B); may be NULL
+ *               when r == 0
  *   bias        bf16 [N] or NULL
  *   Y           [M, N], bf16 (out_dtype = SVDQ_OUT_BF16, round to nearest even) or fp32
  *               (SVDQ_OUT_FP32)                           16B
- *   M >= 0, N >= 1, K % 64 == 0, 64 <= K <= 64 * 65535 (the packer's limit), 0 <= r <= 128,
- *   r % 16 == 0.  The same limits hold for every GEMM entry point below.
+ *   M >= 0, 1 <= N <= 2^24, K % 64 == 0, 64 <= K <= 64 * 65535 (the packer's limit),
+ *   0 <= r <= 128, r % 16 == 0.  The same limits hold for every GEMM entry point below.
  */
 int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
                    const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
@@ -112,7 +122,8 @@ int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
 
 /*
  * svdq_w4a4_partials — test entry: the exact int32 group partials of the same device inner
- * loop as svdq_w4a4_gemm, P[g][m][n] = sum_{k in group g} qx[m, k] qw[n, k].
+ * loop as svdq_w4a4_gemm, P[g][m][n] = sum_{k in group g} qx[m, k] qw[n, k] (the integer dot
+ * products of 4-bit codes that W4A8 2.2 and 4.2 run on the 8-bit units, here one per 64-group).
  *   P  int32 [G, M, N]
  */
 int svdq_w4a4_partials(const uint8_t* xq, const uint8_t* wq, int M, int N, int K, int32_t* P,
@@ -160,7 +171,7 @@ int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N
  *     s = fp16(fl32(amax / 127)),  q = clamp(rne(fl32(x^ / s)), -128, 127),  q = 0 when s == 0,
  * with the smoothing and the low-rank down-projection T of svdq_quantize_act; the weights are
  * those of svdq_pack_weights (INT4 nibbles), and
- *     Y[m, n] = sum_g s_x[g, m] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
+ *     Y[m, n] = sum_g s_x[m, g] s_w[g, n] P[g, m, n] + (bf16(T) L2)[m, n] + bias[n],
  *     P[g, m, n] = sum_{k in group g} q8x[m, k] qw[n, k]   (exact int32).
  * svdq_quantize_act_a8 — svdq_quantize_act writing xq8, int8 [M, K] (two's complement, one code
  *   per byte, 16B) instead of nibbles.
@@ -180,8 +191,9 @@ int svdq_w4a8_partials(const int8_t* xq8, const uint8_t* wq, int M, int N, int K
                        void* stream);
 
 /*
- * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for its
- * cross-token min/max reduction (0 when tokens == 0): the per-part partial ranges and tags of
+ * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for the
+ * cross-token min/max reduction of its per-channel ranges (VARC "INT8 KV cache quantization":
+ * statistics per channel over the cached tokens; 0 when tokens == 0): the per-part partial ranges and tags of
  * the single-pass schedule, or the per-64-token-chunk partials of the three-pass schedule for
  * shapes the single pass does not take; the size covers either.  Its contents need no
  * initialization and carry nothing between calls (a tag left by an earlier call never matches
@@ -206,7 +218,9 @@ int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float
                   uint8_t* zero, void* workspace, void* stream);
 
 /*
- * kv_int8_dequant — x' = bf16(fl32((q - z) * s)) per element (round to nearest even).
+ * kv_int8_dequant — the inverse map of kv_int8_quant's affine code (VARC "INT8 KV cache
+ * quantization": per-channel scale and non-centered zero point),
+ *     x' = bf16(fl32((q - z) * s)) per element (round to nearest even).
  *   q      uint8 [tokens, channels]   16B;   x_out  bf16 [tokens, channels]   16B
  *   scale, zero as written by kv_int8_quant   16B
  *   0 <= tokens <= 2097120 (65535 * 32), channels >= 8, channels % 8 == 0.

@@ -10,6 +10,7 @@ from .workloads import (  # noqa: F401
     LinearConfig,
     bf16_bits_to_f32,
     f64_to_bf16_bits,
+    make_bias,
     make_kv,
     make_linear,
     make_rng,

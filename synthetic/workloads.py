@@ -142,11 +142,15 @@ def make_linear(cid: int, seed: int = 0, M: Optional[int] = None, K: Optional[in
         qv, _ = np.linalg.qr(rs.standard_normal((N, cfg.spike_rank)))
         W += cfg.spike_norm * (qu @ qv.T)
 
-    bias = None
-    if with_bias:
-        bias = f64_to_bf16_bits(make_rng(seed, cid, TAG_BIAS).normal(0.0, 0.1, size=N))
+    bias = make_bias(cid, N, seed) if with_bias else None
     return dict(X=f64_to_bf16_bits(X), W=f64_to_bf16_bits(W), bias=bias,
                 outlier_channels=chans, cfg=cfg, M=M, K=K, N=N)
+
+
+def make_bias(cid: int, N: int, seed: int = 0) -> np.ndarray:
+    """The seeded bias of a linear workload: N(0, 0.1^2) per output column, as bf16 bits (the
+    same values ``make_linear(..., with_bias=True)`` returns)."""
+    return f64_to_bf16_bits(make_rng(seed, cid, TAG_BIAS).normal(0.0, 0.1, size=N))
 
 
 def make_kv(seed: int = 0, tokens: Optional[int] = None, heads: Optional[int] = None,

@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 4
+    assert lib.svdq_abi_version() == 5
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -52,6 +52,16 @@ def test_pack_weights_validation(lib):
     assert lib.svdq_pack_weights(ODD, 64, 8, FAKE, FAKE, None) == binding.SVDQ_EALIGN
     lib.svdq_pack_weights(FAKE, 100, 8, FAKE, FAKE, None)
     assert b"multiple of 64" in lib.svdq_last_error()
+
+
+def test_pack_lowrank_validation(lib):
+    f = lib.svdq_pack_lowrank
+    assert f(FAKE, 100, 16, FAKE, None) == binding.SVDQ_ESHAPE   # K % 64
+    assert f(FAKE, 128, 24, FAKE, None) == binding.SVDQ_ESHAPE   # r % 16
+    assert f(FAKE, 128, 144, FAKE, None) == binding.SVDQ_ESHAPE  # r > 128
+    assert f(FAKE, 128, 0, FAKE, None) == binding.SVDQ_ESHAPE    # nothing to relay out
+    assert f(None, 128, 16, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, 128, 16, None, None) == binding.SVDQ_EINVAL
 
 
 def test_quantize_act_validation(lib):
@@ -75,6 +85,12 @@ def test_gemm_validation(lib):
     assert g(*args, 8, 8, 128, 0, FAKE, 7, None) == binding.SVDQ_EINVAL  # bad out_dtype
     assert g(*args, 8, 8, 128, 24, FAKE, 0, None) == binding.SVDQ_ESHAPE
     assert g(*args, 8, 8, 64 * 65536, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE  # K / 64 > 65535
+    # N beyond 2^24: 32-bit row offsets inside an output tile would wrap
+    assert g(*args, 8, (1 << 24) + 1, 128, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert b"2^24" in lib.svdq_last_error()
+    assert lib.svdq_w4a4_gemm_e3m2(*args, 8, (1 << 24) + 1, 128, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert lib.svdq_w4a8_gemm(*args, 8, (1 << 24) + 1, 128, 0, FAKE, 0, None) == binding.SVDQ_ESHAPE
+    assert lib.svdq_w4a4_partials(FAKE, FAKE, 8, (1 << 24) + 1, 128, FAKE, None) == binding.SVDQ_ESHAPE
     assert g(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 8, 8, 128, 16, FAKE, 0, None) == binding.SVDQ_EINVAL
     assert g(*args, 8, 8, 128, 0, ODD, 0, None) == binding.SVDQ_EALIGN
     assert g(*args, 0, 8, 128, 16, FAKE, 1, None) == binding.SVDQ_OK

@@ -49,10 +49,10 @@ def lib():
 
 def _cases():
     e3 = lambda rows: B.svdq_e3m2_bytes(rows, K)  # noqa: E731
-    act = dict(X=([M, K], bf16), inv_lambda=([K], f32), L1=([R, K], bf16),
-               x_scales=([G, M], f16), T=([M, R], f32))
-    gemm = dict(x_scales=([G, M], f16), T=([M, R], f32), w_scales=([G, N], f16),
-                L2=([N, R], bf16), bias=([N], bf16), Y=([M, N], bf16))
+    act = dict(X=([M, K], bf16), inv_lambda=([K], f32), L1p=([R, K], bf16),
+               x_scales=([M, G], f16), T=([M, R], f32))
+    gemm = dict(x_scales=([M, G], f16), T=([M, R], f32), w_scales=([G, N], f16),
+                L2=([R, N], bf16), bias=([N], bf16), Y=([M, N], bf16))
     kv_t, heads, dim = 70, 2, 64
     C = heads * dim
     return [
@@ -60,11 +60,12 @@ def _cases():
          dict(R=([K, N], f32), wq=([N, K // 2], u8), w_scales=([G, N], f16)), {}),
         (B.svdq_pack_weights_e3m2, ["R", "wq6", "w_scales"],
          dict(R=([K, N], f32), wq6=([e3(N)], u8), w_scales=([G, N], f16)), {}),
-        (B.svdq_quantize_act, ["X", "inv_lambda", "L1", "r", "xq", "x_scales", "T"],
+        (B.svdq_pack_lowrank, ["L1", "L1p"], dict(L1=([K, R], bf16), L1p=([R, K], bf16)), {}),
+        (B.svdq_quantize_act, ["X", "inv_lambda", "L1p", "r", "xq", "x_scales", "T"],
          dict(act, xq=([M, K // 2], u8)), dict(r=R)),
-        (B.svdq_quantize_act_e3m2, ["X", "inv_lambda", "L1", "r", "xq6", "x_scales", "T"],
+        (B.svdq_quantize_act_e3m2, ["X", "inv_lambda", "L1p", "r", "xq6", "x_scales", "T"],
          dict(act, xq6=([e3(M)], u8)), dict(r=R)),
-        (B.svdq_quantize_act_a8, ["X", "inv_lambda", "L1", "r", "xq8", "x_scales", "T"],
+        (B.svdq_quantize_act_a8, ["X", "inv_lambda", "L1p", "r", "xq8", "x_scales", "T"],
          dict(act, xq8=([M, K], i8)), dict(r=R)),
         (B.svdq_w4a4_gemm, ["xq", "x_scales", "T", "wq", "w_scales", "L2", "bias", "r", "Y"],
          dict(gemm, xq=([M, K // 2], u8), wq=([N, K // 2], u8)), dict(r=R)),
@@ -133,8 +134,32 @@ def test_each_wrong_dtype_is_rejected_by_name(case):
         assert f"{fn.__name__}: {want}" in str(e.value), (name, e.value)
 
 
+def _case(fn):
+    return next(c for c in _cases() if c[0] is fn)
+
+
+@pytest.mark.parametrize("fn,name,bad", [
+    (B.svdq_w4a4_gemm, "x_scales", [G, M]),       # group-major instead of [M, K/64]
+    (B.svdq_w4a4_gemm_e3m2, "x_scales", [G, M]),
+    (B.svdq_w4a4_gemm, "L2", [N, R]),             # transposed factor instead of [r, N]
+    (B.svdq_w4a4_gemm_e3m2, "L2", [N, R]),
+    (B.svdq_w4a8_gemm, "T", [R, M]),
+    (B.svdq_quantize_act, "x_scales", [G, M]),
+    (B.svdq_quantize_act, "L1p", [K, R]),          # the unpacked factor
+    (B.svdq_pack_lowrank, "L1p", [K, R]),
+])
+def test_same_size_wrong_shape_is_rejected(fn, name, bad):
+    """A tensor with the right number of bytes but another layout's shape (a transposed factor,
+    group-major scales) is rejected: the library could not tell the layouts apart."""
+    _, order, tensors, scalars = _case(fn)
+    args = _args(order, tensors, scalars)
+    args[order.index(name)] = Dev(bad, tensors[name][1])
+    with pytest.raises(ValueError, match=f"{name} must have shape"):
+        fn(*args)
+
+
 def test_other_device_and_host_tensors_are_rejected():
-    fn, order, tensors, scalars = _cases()[5]  # svdq_w4a4_gemm
+    fn, order, tensors, scalars = _case(B.svdq_w4a4_gemm)
     args = _args(order, tensors, scalars)
     args[order.index("Y")] = Dev(*tensors["Y"], device="cuda:1")
     with pytest.raises(ValueError, match="Y is on cuda:1"):
@@ -146,7 +171,7 @@ def test_other_device_and_host_tensors_are_rejected():
 
 
 def test_output_dtype_must_be_bf16_or_fp32():
-    fn, order, tensors, scalars = _cases()[5]
+    fn, order, tensors, scalars = _case(B.svdq_w4a4_gemm)
     args = _args(order, tensors, scalars)
     args[order.index("Y")] = Dev([M, N], f16)
     with pytest.raises(ValueError, match="bfloat16 or float32"):

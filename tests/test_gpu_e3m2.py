@@ -16,7 +16,7 @@ from bit_post_quantized_amd import binding as B
 from oracle import svdquant as osq
 from oracle.numerics import bf16_to_bits, round_bf16
 from synthetic import make_linear
-from tests.gpu_cases import (FULL, SMALL, dev, dev_bf16, device_weights, host_u16, linear_case,
+from tests.gpu_cases import (oracle_output, FULL, SMALL, dev, dev_bf16, device_weights, host_u16, linear_case,
                              max_abs_rel, oracle_act, with_bias)
 
 pytestmark = pytest.mark.gpu
@@ -53,9 +53,9 @@ def _gpu_act6(case):
     M, K = d["X"].shape
     w = device_weights(case)
     xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r, dtype=torch.float32, device="cuda") if r else None
-    B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), w["inv_lambda"], w["L1t"], r, xq6, xs, T)
+    B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), w["inv_lambda"], w["L1p"], r, xq6, xs, T)
     return xq6, xs, T
 
 
@@ -75,36 +75,27 @@ def test_quantize_act_e3m2_bitexact_codes_and_lowrank(gpu_lib, name):
     torch.cuda.synchronize()
     ref = oracle_act(case)
     np.testing.assert_array_equal(xq6.cpu().numpy(), _expected(name)[1])
-    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"].T).view(np.uint16))
+    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"]).view(np.uint16))
     assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
-
-
-def _rows_for(M, full):
-    if not full:
-        return np.arange(M)
-    rng = np.random.default_rng(123)
-    return np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
-                                     rng.choice(M, 32, replace=False)]))
 
 
 @pytest.mark.parametrize("name,bias", with_bias(CASES))
 def test_gemm_e3m2_output_within_tolerance(gpu_lib, name, bias):
+    """Every row of Y against the oracle's fp64 output, in the launch configuration of the
+    benchmark at the full shapes."""
+    cid, M_, K_, N_ = CASES[name]
     case = _case(name, bias)
     d, pw, packed, r = case
     M = d["X"].shape[0]
     N = pw["R32"].shape[1]
     w = device_weights(case)
-    wq6, ws = _gpu_pack6(case)
-    xq6, xs, T = _gpu_act6(case)
+    wq, ws = _gpu_pack6(case)
+    xq, xs, T = _gpu_act6(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2t"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm_e3m2(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
     torch.cuda.synchronize()
-    ref = oracle_act(case)
-    rows = _rows_for(M, name in FULL)
-    Y_ref = osq.linear_output(ref["codes"][rows], ref["s_x"][rows], packed["codes"],
-                              packed["s_w"], ref["T"][rows] if r else None, pw["L2b"],
-                              d["bias"])
-    err = max_abs_rel(Y.float().cpu().numpy()[rows].astype(np.float64), Y_ref)
+    Y_ref = oracle_output(cid, M_, K_, N_, d["bias"])
+    err = max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref)
     assert err <= TOL, err
 
 
@@ -118,7 +109,7 @@ def test_gemm_e3m2_short_k(gpu_lib, cid, K):
     wq6, ws = _gpu_pack6(case)
     xq6, xs, T = _gpu_act6(case)
     Y = torch.empty(70, 100, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2t"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Y)
     torch.cuda.synchronize()
     ref = oracle_act(case)
     Y_ref = osq.linear_output(ref["codes"], ref["s_x"], packed["codes"], packed["s_w"],
@@ -128,21 +119,28 @@ def test_gemm_e3m2_short_k(gpu_lib, cid, K):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_partials_e3m2_bitexact(gpu_lib, name):
+    """Exact int32 group partials; at the full shapes on the leading 160 x 200 and on the
+    trailing 160 x 192 rows x columns (whole 32-row blocks of each container)."""
     case = _case(name)
     xq6, xs, T = _gpu_act6(case)
     wq6, ws = _gpu_pack6(case)
     d, pw = case[0], case[1]
     (M, K), N = d["X"].shape, pw["R32"].shape[1]
-    if name in FULL:  # the leading rows / columns of the full problem (a prefix of each container)
-        M, N = 160, 200
-        xq6 = xq6[:B.svdq_e3m2_bytes(M, K)]
-        wq6 = wq6[:B.svdq_e3m2_bytes(N, K)]
     G = K // 64
-    P = torch.empty(G, M, N, dtype=torch.int32, device="cuda")
-    B.svdq_w4a4_partials_e3m2(xq6, wq6, M, N, K, P)
-    torch.cuda.synchronize()
     ref = oracle_act(case)
-    np.testing.assert_array_equal(P.cpu().numpy(), osq.int_partials(ref["codes"][:M], case[2]["codes"][:N]))
+    blk = G * 1536  # bytes of one 32-row block of a container
+    parts = [(0, M, 0, N)]
+    if name in FULL:
+        assert (M - 160) % 32 == 0 and (N - 192) % 32 == 0
+        parts = [(0, 160, 0, 200), (M - 160, 160, N - 192, 192)]
+    for m0, mm, n0, nn in parts:
+        xs6 = xq6[(m0 // 32) * blk:(m0 // 32) * blk + B.svdq_e3m2_bytes(mm, K)]
+        ws6 = wq6[(n0 // 32) * blk:(n0 // 32) * blk + B.svdq_e3m2_bytes(nn, K)]
+        P = torch.empty(G, mm, nn, dtype=torch.int32, device="cuda")
+        B.svdq_w4a4_partials_e3m2(xs6, ws6, mm, nn, K, P)
+        torch.cuda.synchronize()
+        P_ref = osq.int_partials(ref["codes"][m0:m0 + mm], case[2]["codes"][n0:n0 + nn])
+        np.testing.assert_array_equal(P.cpu().numpy(), P_ref)
 
 
 @pytest.mark.parametrize("K", [64, 192, 320])  # G = 1, 3, 5: the last stage holds one group
@@ -167,9 +165,9 @@ def test_e3m2_and_nibble_routes_agree(gpu_lib):
     w = device_weights(case)
     K = d["X"].shape[1]
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r, dtype=torch.float32, device="cuda")
-    B.svdq_quantize_act(dev_bf16(d["X"]), w["inv_lambda"], w["L1t"], r, xq, xs, T)
+    B.svdq_quantize_act(dev_bf16(d["X"]), w["inv_lambda"], w["L1p"], r, xq, xs, T)
     wq = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
     B.svdq_pack_weights(w["R32"], wq, ws)
@@ -177,8 +175,8 @@ def test_e3m2_and_nibble_routes_agree(gpu_lib):
     wq6, ws6 = _gpu_pack6(case)
     Y4 = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Y6 = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2t"], w["bias"], r, Y4)
-    B.svdq_w4a4_gemm_e3m2(xq6, xs6, T6, wq6, ws6, w["L2t"], w["bias"], r, Y6)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y4)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs6, T6, wq6, ws6, w["L2"], w["bias"], r, Y6)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(osq.unpack_e3m2_tiled(xq6.cpu().numpy(), M, K), osq.unpack_nibbles(xq.cpu().numpy()))
     np.testing.assert_array_equal(osq.unpack_e3m2_tiled(wq6.cpu().numpy(), N, K), osq.unpack_nibbles(wq.cpu().numpy()))
@@ -199,7 +197,7 @@ def test_e3m2_rank0_unit_scales_reduce_to_exact_integer_gemm(gpu_lib):
     exact = X @ Wt.T
     inv = torch.ones(K, dtype=torch.float32, device="cuda")
     xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act_e3m2(dev_bf16(bf16_to_bits(X)), inv, None, 0, xq6, xs, None)
     wq6 = torch.empty(B.svdq_e3m2_bytes(N, K), dtype=torch.uint8, device="cuda")
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
@@ -229,10 +227,10 @@ def test_e3m2_clamped_codes_of_subnormal_scales(gpu_lib):
     ref = osq.quantize_act(bits, inv, None)
     assert (ref["codes"] == -8).sum() >= M * K // 64 and float(ref["s_x"].max()) == 2.0 ** -24
     xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act_e3m2(dev_bf16(bits), dev(inv), None, 0, xq6, xs, None)
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-    xs4 = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs4 = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act(dev_bf16(bits), dev(inv), None, 0, xq, xs4, None)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(xq6.cpu().numpy(), osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
@@ -256,12 +254,12 @@ def test_e3m2_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     xs = torch.full((G * M + 8,), -3.0, dtype=torch.float16, device="cuda")
     T = torch.full((M + 1, max(r, 1)), -7.0, dtype=torch.float32, device="cuda")
     L1t = dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None
-    L2t = dev_bf16(bf16_to_bits(pw["L2b"].T)) if r else None
+    L2t = dev_bf16(bf16_to_bits(pw["L2b"])) if r else None  # [r, N]
     Tv = T[:M] if r else None
     B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq6[:BX],
-                             xs[:G * M].view(G, M), Tv)
+                             xs[:G * M].view(M, G), Tv)
     Y = torch.full((M + 1, N), 3.0, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6[:BX], xs[:G * M].view(G, M), Tv, wq6[:BW], ws[:G * N].view(G, N),
+    B.svdq_w4a4_gemm_e3m2(xq6[:BX], xs[:G * M].view(M, G), Tv, wq6[:BW], ws[:G * N].view(G, N),
                           L2t, dev_bf16(d["bias"]), r, Y[:M])
     torch.cuda.synchronize()
     np.testing.assert_array_equal(wq6[:BW].cpu().numpy(), osq.pack_e3m2_tiled(packed["codes"]).reshape(-1))
@@ -285,8 +283,8 @@ def test_e3m2_fp32_output_and_determinism(gpu_lib):
     xq6, xs, T = _gpu_act6(case)
     Ya = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Yb = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2t"], w["bias"], r, Ya)
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2t"], w["bias"], r, Yb)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Ya)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Yb)
     torch.cuda.synchronize()
     assert torch.equal(Ya, Yb)
     ref = oracle_act(case)

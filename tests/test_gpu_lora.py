@@ -32,12 +32,12 @@ def test_lora_branch_parity(gpu_lib, rl, e3m2):
                               L2p, d["bias"])
 
     L1t = dev_bf16(bf16_to_bits(L1p.T))
-    L2t = dev_bf16(bf16_to_bits(L2p.T))
+    L2t = dev_bf16(bf16_to_bits(L2p))  # [r, N]
     inv = dev(pw["inv_lambda"])
     R32 = dev(pw["R32"])
     bias = dev_bf16(d["bias"])
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r2, dtype=torch.float32, device="cuda")
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     X = dev_bf16(d["X"])
@@ -57,7 +57,7 @@ def test_lora_branch_parity(gpu_lib, rl, e3m2):
         want_xq = ref["xq"]
     torch.cuda.synchronize()
     np.testing.assert_array_equal(xq.cpu().numpy(), want_xq)
-    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"].T).view(np.uint16))
+    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"]).view(np.uint16))
     assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
     assert max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref) <= TOL
     # the adapter really changed the output (its term is not lost in the tolerance)

@@ -14,7 +14,7 @@ from oracle import kv_int8 as okv
 from oracle import svdquant as osq
 from oracle.numerics import bf16_to_bits, round_bf16
 from synthetic import make_linear
-from tests.gpu_cases import (FULL, SMALL, dev, dev_bf16, device_weights, host_u16, kv_case,
+from tests.gpu_cases import (oracle_output, FULL, SMALL, dev, dev_bf16, device_weights, host_u16, kv_case,
                              linear_case, max_abs_rel, oracle_act, with_bias)
 
 pytestmark = pytest.mark.gpu
@@ -43,9 +43,9 @@ def _gpu_act(case):
     w = device_weights(case)
     X = dev_bf16(d["X"])
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r, dtype=torch.float32, device="cuda") if r else None
-    B.svdq_quantize_act(X, w["inv_lambda"], w["L1t"], r, xq, xs, T)
+    B.svdq_quantize_act(X, w["inv_lambda"], w["L1p"], r, xq, xs, T)
     return xq, xs, T
 
 
@@ -66,7 +66,7 @@ def test_quantize_act_bitexact_codes_and_lowrank(gpu_lib, name):
     torch.cuda.synchronize()
     ref = oracle_act(case)
     np.testing.assert_array_equal(xq.cpu().numpy(), ref["xq"])
-    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"].T).view(np.uint16))
+    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"]).view(np.uint16))
     err = max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"])
     assert err <= TOL, err
 
@@ -83,66 +83,60 @@ def test_quantize_act_long_k_both_containers(gpu_lib):
     ref = oracle_act(case)
     xq, xs, T = _gpu_act(case)
     xq6 = torch.empty(B.svdq_e3m2_bytes(M, K), dtype=torch.uint8, device="cuda")
-    xs6 = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs6 = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T6 = torch.empty(M, r, dtype=torch.float32, device="cuda")
-    B.svdq_quantize_act_e3m2(X, w["inv_lambda"], w["L1t"], r, xq6, xs6, T6)
+    B.svdq_quantize_act_e3m2(X, w["inv_lambda"], w["L1p"], r, xq6, xs6, T6)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(xq.cpu().numpy(), ref["xq"])
     np.testing.assert_array_equal(xq6.cpu().numpy(), osq.pack_e3m2_tiled(ref["codes"]).reshape(-1))
-    want_s = np.ascontiguousarray(ref["s_x"].T).view(np.uint16)
+    want_s = np.ascontiguousarray(ref["s_x"]).view(np.uint16)
     np.testing.assert_array_equal(host_u16(xs), want_s)
     np.testing.assert_array_equal(host_u16(xs6), want_s)
     assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
     assert max_abs_rel(T6.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
 
 
-def _rows_for(M, full):
-    if not full:
-        return np.arange(M)
-    rng = np.random.default_rng(123)
-    return np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
-                                     rng.choice(M, 32, replace=False)]))
-
-
 @pytest.mark.parametrize("name,bias", with_bias(CASES))
 def test_gemm_output_within_tolerance(gpu_lib, name, bias):
+    """Every row of Y against the oracle's fp64 output, in the launch configuration of the
+    benchmark at the full shapes."""
+    cid, M_, K_, N_ = CASES[name]
     case = _case(name, bias)
     d, pw, packed, r = case
-    M, K = d["X"].shape
+    M = d["X"].shape[0]
     N = pw["R32"].shape[1]
     w = device_weights(case)
     wq, ws = _gpu_pack(case)
     xq, xs, T = _gpu_act(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2t"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
     torch.cuda.synchronize()
-    ref = oracle_act(case)
-    rows = _rows_for(M, name in FULL)
-    Y_ref = osq.linear_output(ref["codes"][rows], ref["s_x"][rows], packed["codes"],
-                              packed["s_w"], ref["T"][rows] if r else None, pw["L2b"],
-                              d["bias"])
-    got = Y.float().cpu().numpy()[rows].astype(np.float64)
-    err = max_abs_rel(got, Y_ref)
+    Y_ref = oracle_output(cid, M_, K_, N_, d["bias"])
+    err = max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref)
     assert err <= TOL, err
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_partials_bitexact(gpu_lib, name):
+    """Exact int32 group partials; at the full shapes (whose G M N partials do not fit in
+    memory) on the leading and on the trailing 160 rows x 200 columns of the problem."""
     case = _case(name)
     d, pw, packed, r = case
     xq, xs, T = _gpu_act(case)
     wq, ws = _gpu_pack(case)
-    M, N = xq.shape[0], wq.shape[0]
-    if name in FULL:  # a row/column slice of the full problem (same kernel, same k loop)
-        M, N = 160, 200
-        xq, wq = xq[:M].contiguous(), wq[:N].contiguous()
-    G = xq.shape[1] * 2 // 64
-    P = torch.empty(G, M, N, dtype=torch.int32, device="cuda")
-    B.svdq_w4a4_partials(xq, wq, P)
-    torch.cuda.synchronize()
     ref = oracle_act(case)
-    P_ref = osq.int_partials(ref["codes"][:M], packed["codes"][:N])
-    np.testing.assert_array_equal(P.cpu().numpy(), P_ref)
+    M, N = xq.shape[0], wq.shape[0]
+    slices = [(slice(0, M), slice(0, N))]
+    if name in FULL:
+        slices = [(slice(0, 160), slice(0, 200)), (slice(M - 160, M), slice(N - 200, N))]
+    for rs, cs in slices:
+        xs_, ws_ = xq[rs].contiguous(), wq[cs].contiguous()
+        G = xs_.shape[1] * 2 // 64
+        P = torch.empty(G, xs_.shape[0], ws_.shape[0], dtype=torch.int32, device="cuda")
+        B.svdq_w4a4_partials(xs_, ws_, P)
+        torch.cuda.synchronize()
+        P_ref = osq.int_partials(ref["codes"][rs], packed["codes"][cs])
+        np.testing.assert_array_equal(P.cpu().numpy(), P_ref)
 
 
 def test_rank0_unit_scales_reduce_to_exact_integer_gemm(gpu_lib):
@@ -161,7 +155,7 @@ def test_rank0_unit_scales_reduce_to_exact_integer_gemm(gpu_lib):
     Xd = dev_bf16(bf16_to_bits(X))
     inv = torch.ones(K, dtype=torch.float32, device="cuda")
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act(Xd, inv, None, 0, xq, xs, None)
     wq = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda")
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
@@ -193,7 +187,7 @@ def test_exact_ties_round_half_to_even(gpu_lib):
     inv = np.ones(K, np.float32)
     ref = osq.quantize_act(bits, inv, None)
     xq = torch.empty(M, K // 2, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     B.svdq_quantize_act(dev_bf16(bits), dev(inv), None, 0, xq, xs, None)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(xq.cpu().numpy(), ref["xq"])
@@ -216,12 +210,12 @@ def test_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     xs = torch.full((G * M + 8,), -3.0, dtype=torch.float16, device="cuda")
     T = torch.full((M + 1, max(r, 1)), -7.0, dtype=torch.float32, device="cuda")
     L1t = dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None
-    L2t = dev_bf16(bf16_to_bits(pw["L2b"].T)) if r else None
+    L2t = dev_bf16(bf16_to_bits(pw["L2b"])) if r else None  # [r, N]
     Tv = T[:M] if r else None
     B.svdq_quantize_act(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq[:M],
-                        xs[:G * M].view(G, M), Tv)
+                        xs[:G * M].view(M, G), Tv)
     Y = torch.full((M + 1, N), 3.0, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm(xq[:M], xs[:G * M].view(G, M), Tv, wq[:N], ws[:G * N].view(G, N), L2t,
+    B.svdq_w4a4_gemm(xq[:M], xs[:G * M].view(M, G), Tv, wq[:N], ws[:G * N].view(G, N), L2t,
                      dev_bf16(d["bias"]), r, Y[:M])
     torch.cuda.synchronize()
     np.testing.assert_array_equal(wq[:N].cpu().numpy(), packed["wq"])
@@ -246,9 +240,9 @@ def test_fp32_output_and_determinism(gpu_lib):
     xq, xs, T = _gpu_act(case)
     Ya = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Yb = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2t"], w["bias"], r, Ya)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Ya)
     xq2, xs2, T2 = _gpu_act(case)
-    B.svdq_w4a4_gemm(xq2, xs2, T2, wq, ws, w["L2t"], w["bias"], r, Yb)
+    B.svdq_w4a4_gemm(xq2, xs2, T2, wq, ws, w["L2"], w["bias"], r, Yb)
     torch.cuda.synchronize()
     assert torch.equal(Ya, Yb) and torch.equal(T, T2)
     ref = oracle_act(case)

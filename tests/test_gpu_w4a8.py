@@ -29,9 +29,9 @@ def _gpu(case):
     ws = torch.empty(K // 64, N, dtype=torch.float16, device="cuda")
     B.svdq_pack_weights(w["R32"], wq, ws)
     xq8 = torch.empty(M, K, dtype=torch.int8, device="cuda")
-    xs = torch.empty(K // 64, M, dtype=torch.float16, device="cuda")
+    xs = torch.empty(M, K // 64, dtype=torch.float16, device="cuda")
     T = torch.empty(M, r, dtype=torch.float32, device="cuda") if r else None
-    B.svdq_quantize_act_a8(dev_bf16(d["X"]), w["inv_lambda"], w["L1t"], r, xq8, xs, T)
+    B.svdq_quantize_act_a8(dev_bf16(d["X"]), w["inv_lambda"], w["L1p"], r, xq8, xs, T)
     return w, wq, ws, xq8, xs, T
 
 
@@ -43,7 +43,7 @@ def test_act_a8_codes_scales_and_lowrank(gpu_lib, name):
     torch.cuda.synchronize()
     ref = osq.quantize_act_a8(d["X"], pw["inv_lambda"], pw["L1b"])
     np.testing.assert_array_equal(xq8.cpu().numpy(), ref["xq8"])
-    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"].T).view(np.uint16))
+    np.testing.assert_array_equal(host_u16(xs), np.ascontiguousarray(ref["s_x"]).view(np.uint16))
     assert max_abs_rel(T.cpu().numpy().astype(np.float64), ref["T"]) <= TOL
 
 
@@ -55,7 +55,7 @@ def test_w4a8_gemm_output_within_tolerance(gpu_lib, name, bias):
     N = pw["R32"].shape[1]
     w, wq, ws, xq8, xs, T = _gpu(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a8_gemm(xq8, xs, T, wq, ws, w["L2t"], w["bias"], r, Y)
+    B.svdq_w4a8_gemm(xq8, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
     torch.cuda.synchronize()
     ref = osq.quantize_act_a8(d["X"], pw["inv_lambda"], pw["L1b"])
     if name in FULL:
@@ -93,7 +93,7 @@ def test_w4a8_extreme_codes_and_fp32_output(gpu_lib):
     xq8 = torch.from_numpy(cx).cuda()
     wq = torch.from_numpy(osq.pack_nibbles(cw)).cuda()
     one = np.float16(1.0).view(np.uint16)
-    xs = torch.from_numpy(np.full((K // 64, M), one, np.uint16).view(np.int16)).view(torch.float16).cuda()
+    xs = torch.from_numpy(np.full((M, K // 64), one, np.uint16).view(np.int16)).view(torch.float16).cuda()
     ws = torch.from_numpy(np.full((K // 64, N), one, np.uint16).view(np.int16)).view(torch.float16).cuda()
     Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
     B.svdq_w4a8_gemm(xq8, xs, None, wq, ws, None, None, 0, Y)
