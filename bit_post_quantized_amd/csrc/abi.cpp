@@ -263,6 +263,21 @@ int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float
                     "kv_int8_quant");
 }
 
+int kv_int8_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                       uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv, uint8_t* zv,
+                       void* workspace, void* stream) {
+  if (int s = check_kv(tokens, channels)) return s;
+  if (!k || !v || !qk || !sk || !zk || !qv || !sv || !zv || (tokens > 0 && !workspace))
+    return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(qk) || !aligned16(sk) || !aligned16(zk) ||
+      !aligned16(qv) || !aligned16(sv) || !aligned16(zv) || !aligned16(workspace))
+    return fail(SVDQ_EALIGN, "tensors and workspace must be 16-byte aligned");
+  if (tokens == 0) return ok();
+  return hip_status(svdq::launch_kv_quant_pair(k, v, tokens, channels, qk, sk, zk, qv, sv, zv,
+                                               workspace, (hipStream_t)stream),
+                    "kv_int8_quant_pair");
+}
+
 int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
                     int channels, uint16_t* x_out, void* stream) {
   if (int s = check_kv(tokens, channels)) return s;

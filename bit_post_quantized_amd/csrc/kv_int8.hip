@@ -305,13 +305,25 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const uint8_t* __restri
 // range is agreed, then codes it from registers.  A slab of 128 channels (256 bytes of a bf16
 // row, one whole 128-byte line of its codes) is split over kFusedParts blocks by tokens (a
 // 64-channel slab writes half lines, which two XCDs then write back separately, and loads
-// 128-byte strips; both measured slower); each block folds min / max over its
-// tokens, publishes the partial range in the workspace with the call's epoch as a tag, waits
-// for the other parts' tags, folds the parts, and quantizes.  The parts of a slab are mapped
-// to blocks that the dispatcher places on one XCD (block b runs on XCD b % 8), so the exchange
-// mostly stays in one L2.  The wait is bounded: a block that times out (e.g. when not every
-// part of its slab is resident) computes the slab's range from x itself, so the result never
-// depends on the exchange and the kernel always finishes.
+// 128-byte strips; both measured slower); each block folds min / max over its tokens,
+// publishes the partial range in the workspace, reads the other parts' ranges, folds them, and
+// quantizes.  The parts of a slab are mapped to blocks that the dispatcher places on one XCD
+// (block b runs on XCD b % 8).
+//
+// The exchange needs no fence.  Every published word is one 64-bit relaxed atomic store at
+// agent scope holding (call epoch, float bits); a reader accepts a word only when it carries
+// the running call's epoch.  Each word is validated by itself (a single location is coherent,
+// and a 64-bit atomic is never seen torn), so no ordering between words, waves or blocks is
+// needed.  (The first design published plain stores behind release fences; on this device an
+// agent-scope release writes back the XCD's L2, which took 6.5 to 9 us per exchange out of a
+// 30 us call.)  The wait is bounded: a block whose wait times out (e.g. when not every part of
+// its slab is resident) computes the slab's range from x itself, so the result never depends
+// on the exchange and the kernel always finishes.
+//
+// The paired form quantizes two tensors of one shape (a layer's K and V) in one launch: once a
+// block has the first tensor's parameters it stores each row's codes and loads the second
+// tensor's row into the registers that row held; then the second tensor's range is agreed and
+// its codes written as in the single form.
 constexpr int kFusedCh = 128;
 constexpr int kFusedParts = 8;
 constexpr int kFusedThreads = 512;
@@ -321,6 +333,16 @@ constexpr int kFusedMaxRows = 40;                                     // rows pe
 constexpr int kFusedSegs = kFusedThreads / kFusedCh;                  // 4 fold segments of 8 rows
 static_assert(kFusedSegs * 8 == kFusedRowsPerPass, "block fold: segments of 8 rows");
 constexpr int kFusedInFlight = 8;                                     // row loads in flight
+// row loads in flight while the paired form stores the first tensor's codes (the stores count
+// in the same in-order counter as the loads, so a wait for a load also waits for every store
+// issued before it)
+constexpr int kPairInFlight = 8;
+// workspace of one tensor: per part of a slab, 2 x 128 words (lo, hi) of (epoch << 32 | bits)
+constexpr size_t kFusedPartBytes = 2 * kFusedCh * sizeof(uint64_t);
+
+__host__ __device__ inline size_t fused_region_bytes(int channels) {
+  return (size_t)(channels / kFusedCh) * kFusedParts * kFusedPartBytes;
+}
 
 __device__ __forceinline__ void fused_slab_part(int b, int nslabs, int& slab, int& part) {
   if (nslabs % 8 == 0) {  // the kFusedParts blocks of a slab share XCD b % 8
@@ -333,14 +355,148 @@ __device__ __forceinline__ void fused_slab_part(int b, int nslabs, int& slab, in
   }
 }
 
-template <int R>  // token rows per thread held in registers
+// One tensor of a fused call: its rows, outputs, and its region of the workspace (the parts'
+// published partial ranges, [slab][part][lo 128 | hi 128] words).
+struct KvFusedTensor {
+  const uint16_t* x;
+  uint8_t* q;
+  float* scale;
+  uint8_t* zero;
+  uint64_t* parts;
+};
+
+struct KvFusedShared {
+  float stage[2][kFusedRowsPerPass][kFusedCh + 1];
+  float red[2][kFusedSegs][kFusedCh];
+  float prm[3][kFusedCh];  // s, 1 / s, z of the slab's channels
+};
+
+// Block-wide min / max of the slab's channels over this block's rows: thread (rr, lc) holds the
+// range of its 8 channels over its rows; on return threads 0..127 hold channel tid's range.
+__device__ __forceinline__ void fused_block_fold(KvFusedShared& sh, const float* lo,
+                                                 const float* hi, float& out_lo, float& out_hi) {
+  const int tid = threadIdx.x;
+  const int lc = tid % kFusedRowThreads, rr = tid / kFusedRowThreads;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    sh.stage[0][rr][lc * 8 + i] = lo[i];
+    sh.stage[1][rr][lc * 8 + i] = hi[i];
+  }
+  __syncthreads();
+  {
+    const int ch = tid % kFusedCh, seg = tid / kFusedCh;  // segments of 8 rows
+    float l = 0.0f, h = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      l = __builtin_fminf(l, sh.stage[0][seg * 8 + k][ch]);
+      h = __builtin_fmaxf(h, sh.stage[1][seg * 8 + k][ch]);
+    }
+    sh.red[0][seg][ch] = l;
+    sh.red[1][seg][ch] = h;
+  }
+  __syncthreads();
+  if (tid < kFusedCh) {
+    float l = 0.0f, h = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kFusedSegs; ++k) {
+      l = __builtin_fminf(l, sh.red[0][k][tid]);
+      h = __builtin_fmaxf(h, sh.red[1][k][tid]);
+    }
+    out_lo = l;
+    out_hi = h;
+  }
+}
+
+__device__ __forceinline__ uint64_t tagged(uint32_t epoch, float v) {
+  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+
+// From this block's folded range (lo / hi of the thread's 8 channels) to the slab's parameters
+// in sh.prm: publish the part's range, read every part's range once it carries this call's
+// epoch (bounded wait), fold them; on a time-out, the slab's range straight from x.  Part 0
+// stores the slab's scale and zero.
+__device__ __forceinline__ void fused_slab_params(KvFusedShared& sh, const KvFusedTensor& T,
+                                               float* lo, float* hi, int tokens, int channels,
+                                               int slab, int part, uint32_t epoch,
+                                               long long spin_ticks) {
+  const int tid = threadIdx.x;
+  const int lc = tid % kFusedRowThreads, rr = tid / kFusedRowThreads;
+  const int c0 = slab * kFusedCh + lc * kKvLanesC;
+  float plo = 0.0f, phi = 0.0f;
+  fused_block_fold(sh, lo, hi, plo, phi);
+
+  int timed_out = 0;
+  if (tid < kFusedCh) {  // thread tid owns channel tid of the slab: waves 0 and 1
+    uint64_t* all = T.parts + (size_t)slab * kFusedParts * 2 * kFusedCh;
+    uint64_t* mine = all + (size_t)part * 2 * kFusedCh;
+    __hip_atomic_store(mine + tid, tagged(epoch, plo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + kFusedCh + tid, tagged(epoch, phi), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    // every part's (lo, hi) of channel tid, 16 loads per poll; parts already seen are kept
+    uint64_t w[2 * kFusedParts];
+    uint32_t pending = (1u << (2 * kFusedParts)) - 1u;
+    const long long start = wall_clock64();
+    for (;;) {
+#pragma unroll
+      for (int i = 0; i < 2 * kFusedParts; ++i)
+        if (pending & (1u << i))
+          w[i] = __hip_atomic_load(all + (size_t)(i >> 1) * 2 * kFusedCh + (i & 1) * kFusedCh + tid,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int i = 0; i < 2 * kFusedParts; ++i)
+        if ((uint32_t)(w[i] >> 32) == epoch) pending &= ~(1u << i);
+      if (pending == 0u) break;
+      if (wall_clock64() - start > spin_ticks) {
+        timed_out = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!timed_out) {
+      float l = 0.0f, h = 0.0f;
+#pragma unroll
+      for (int p = 0; p < kFusedParts; ++p) {
+        l = __builtin_fminf(l, __uint_as_float((uint32_t)w[2 * p]));
+        h = __builtin_fmaxf(h, __uint_as_float((uint32_t)w[2 * p + 1]));
+      }
+      plo = l;
+      phi = h;
+    }
+  }
+  if (__syncthreads_or(timed_out)) {
+    // the slab's range straight from x: every token, one pass of rows after the other
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0.0f;
+    for (int t = rr; t < tokens; t += kFusedRowsPerPass) {
+      float f[8];
+      decode8_bf16(*reinterpret_cast<const v4u*>(T.x + (size_t)t * channels + c0), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = __builtin_fminf(lo[i], f[i]);
+        hi[i] = __builtin_fmaxf(hi[i], f[i]);
+      }
+    }
+    fused_block_fold(sh, lo, hi, plo, phi);
+  }
+  if (tid < kFusedCh) {
+    float s, z;
+    params_from_range(plo, phi, s, z);
+    sh.prm[0][tid] = s;
+    sh.prm[1][tid] = 1.0f / s;
+    sh.prm[2][tid] = z;
+    if (part == 0) {
+      T.scale[slab * kFusedCh + tid] = s;
+      T.zero[slab * kFusedCh + tid] = (uint8_t)z;
+    }
+  }
+  __syncthreads();
+}
+
+template <int R, bool kPair>  // token rows per thread held in registers; two tensors or one
 __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
-    const uint16_t* __restrict__ x, int tokens, int channels, uint8_t* __restrict__ q,
-    float* __restrict__ scale, uint8_t* __restrict__ zero, uint32_t* __restrict__ tags,
-    float* __restrict__ parts, uint32_t epoch, long long spin_ticks) {
-  __shared__ float red[2][kFusedSegs][kFusedCh];
-  __shared__ float prm[3][kFusedCh];  // s, 1 / s, z
-  __shared__ int fallback;
+    KvFusedTensor a, KvFusedTensor b, int tokens, int channels, uint32_t epoch,
+    long long spin_ticks) {
+  __shared__ KvFusedShared sh;
   const int nslabs = channels / kFusedCh;
   int slab, part;
   fused_slab_part(blockIdx.x, nslabs, slab, part);
@@ -349,19 +505,29 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
   const int c0 = slab * kFusedCh + lc * kKvLanesC;
   const int per = (tokens + kFusedParts - 1) / kFusedParts;
   const int t0 = part * per, t1 = min(tokens, t0 + per);
+  // Rows t0 + rr + 32 k, k < nk, are this thread's: one live count and one moving pointer per
+  // stream.  (A token index per row does not fit beside the rows; a spilled one costs a wait on
+  // every row, because stores count in the same counter as the spill reload.)  Loads clamp the
+  // row index into the tensor: a duplicate row leaves min / max unchanged.
+  const int nk = max(0, (t1 - t0 - rr + kFusedRowsPerPass - 1) / kFusedRowsPerPass);
+  const size_t pass = (size_t)kFusedRowsPerPass * channels;
+  auto row_of = [&](const uint16_t* x, int k) {
+    return reinterpret_cast<const v4u*>(
+        x + (size_t)min(t0 + rr + kFusedRowsPerPass * k, tokens - 1) * channels + c0);
+  };
 
-  // ---- load this thread's rows (row index clamped into the tensor: a duplicate row leaves
-  //      min / max unchanged) and fold min / max of its 8 channels
+  // ---- load this thread's rows of the first tensor
   // At most kFusedInFlight rows of a thread are in flight: with every row of the grid requested
   // at once the memory system serves some waves far later than the others, and every block
   // waits for the slowest part of its slab.
   v4u v[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const int t = min(t0 + rr + kFusedRowsPerPass * k, tokens - 1);
-    v[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + (size_t)t * channels + c0));
+    v[k] = __builtin_nontemporal_load(row_of(a.x, k));
     if (k >= kFusedInFlight) asm volatile("" : "+v"(v[k - kFusedInFlight])::"memory");
   }
+  // min / max of the thread's 8 channels over its rows (written out here: a helper or lambda
+  // that takes the row array by reference leaves it in scratch memory)
   float lo[8], hi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0.0f;
@@ -375,144 +541,72 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
       hi[i] = __builtin_fmaxf(hi[i], f[i]);
     }
   }
-  // block fold: kFusedRowsPerPass row-threads per channel -> segments of 8 rows in LDS -> 1
-  auto block_fold = [&](float* out_lo, float* out_hi) {
-    __shared__ float stage[2][kFusedRowsPerPass][kFusedCh + 1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      stage[0][rr][lc * 8 + i] = lo[i];
-      stage[1][rr][lc * 8 + i] = hi[i];
-    }
-    __syncthreads();
-    {
-      const int ch = tid % kFusedCh, seg = tid / kFusedCh;  // segments of 8 rows
-      float l = 0.0f, h = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        l = __builtin_fminf(l, stage[0][seg * 8 + k][ch]);
-        h = __builtin_fmaxf(h, stage[1][seg * 8 + k][ch]);
-      }
-      red[0][seg][ch] = l;
-      red[1][seg][ch] = h;
-    }
-    __syncthreads();
-    if (tid < kFusedCh) {
-      float l = 0.0f, h = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kFusedSegs; ++k) {
-        l = __builtin_fminf(l, red[0][k][tid]);
-        h = __builtin_fmaxf(h, red[1][k][tid]);
-      }
-      *out_lo = l;
-      *out_hi = h;
-    }
-  };
-  float plo = 0.0f, phi = 0.0f;
-  block_fold(&plo, &phi);
   // keep only the packed rows live across the exchange (the codes decode them again)
 #pragma unroll
   for (int k = 0; k < R; ++k) asm volatile("" : "+v"(v[k]));
+  fused_slab_params(sh, a, lo, hi, tokens, channels, slab, part, epoch, spin_ticks);
 
-  // ---- publish this part's range, then wait (bounded) for the other parts
-  // Publication order: waves 0 and 1 store the part's range (channels 0..63 and 64..127); each
-  // of them releases its own stores at agent scope before the barrier, so both halves are
-  // visible device-wide before any wave passes the barrier, and so before thread 0's
-  // release store of the tag that the other parts acquire.  (The tag's release alone orders
-  // only the stores of the wave that issues it.)
-  float* mine = parts + ((size_t)slab * kFusedParts + part) * 2 * kFusedCh;
-  if (tid < kFusedCh) {  // whole waves 0 and 1
-    mine[tid] = plo;
-    mine[kFusedCh + tid] = phi;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  }
-  __syncthreads();
-  if (tid < 64) {  // wave 0: lane p < kFusedParts watches part p's tag
-    if (tid == 0)
-      __hip_atomic_store(tags + slab * kFusedParts + part, epoch, __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    int fb = 0;
-    const long long start = wall_clock64();
-    // relaxed polling of all the tags at once, one round trip per poll (an acquire per poll
-    // would invalidate caches on every iteration; tags polled one after the other cost one
-    // round trip each: 4.8 us from the slowest part's publication to the exchange's end);
-    // the acquire fence after the wait orders the reads of the partial ranges
-    for (;;) {
-      const bool seen = tid >= kFusedParts ||
-                        __hip_atomic_load(tags + slab * kFusedParts + tid, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == epoch;
-      if (__all(seen)) break;  // uniform over the wave
-      if (wall_clock64() - start > spin_ticks) {
-        fb = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    // one acquire (it invalidates the CU's vector cache, which every wave shares) before the
-    // barrier after which the partial ranges are read
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (tid == 0) fallback = fb;
-  }
-  __syncthreads();
-  if (!fallback) {
-    if (tid < kFusedCh) {
-      float l = 0.0f, h = 0.0f;
-      const float* all = parts + (size_t)slab * kFusedParts * 2 * kFusedCh;
+  float s8[8], r8[8], z8[8];
 #pragma unroll
-      for (int p = 0; p < kFusedParts; ++p) {
-        l = __builtin_fminf(l, __hip_atomic_load(all + p * 2 * kFusedCh + tid, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT));
-        h = __builtin_fmaxf(h, __hip_atomic_load(all + p * 2 * kFusedCh + kFusedCh + tid,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      }
-      plo = l;
-      phi = h;
+  for (int i = 0; i < 8; ++i) {
+    s8[i] = sh.prm[0][lc * 8 + i];
+    r8[i] = sh.prm[1][lc * 8 + i];
+    z8[i] = sh.prm[2][lc * 8 + i];
+  }
+  uint8_t* qp = a.q + (size_t)(t0 + rr) * channels + c0;
+  if constexpr (!kPair) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (k < nk) __builtin_nontemporal_store(quant_row8(v[k], s8, r8, z8), reinterpret_cast<v2u*>(qp));
+      qp += pass;
     }
   } else {
-    // the slab's range straight from x: every token, one pass of rows after the other
+    // ---- codes of the first tensor, each row's register refilled with the second's row
+    // The second tensor's rows come from a moving pointer (rows past the tensor's end read its
+    // last row, as row_of does), kept opaque so that the compiler does not precompute every
+    // row's address ahead of the loop: those addresses would not fit beside the rows.
+    const uint16_t* xb = b.x + (size_t)(t0 + rr) * channels + c0;
+    const uint16_t* const xlast = b.x + (size_t)(tokens - 1) * channels + c0;
+    const int rem = tokens - 1 - t0 - rr;
+    const int klast = rem < 0 ? -1 : rem / kFusedRowsPerPass;  // last row k inside the tensor
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (k < nk) __builtin_nontemporal_store(quant_row8(v[k], s8, r8, z8), reinterpret_cast<v2u*>(qp));
+      qp += pass;
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(k <= klast ? xb : xlast));
+      xb += pass;
+      asm volatile("" : "+v"(xb));
+      if (k >= kPairInFlight) asm volatile("" : "+v"(v[k - kPairInFlight])::"memory");
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0.0f;
-    for (int t = rr; t < tokens; t += kFusedRowsPerPass) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
       float f[8];
-      decode8_bf16(*reinterpret_cast<const v4u*>(x + (size_t)t * channels + c0), f);
+      decode8_bf16(v[k], f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         lo[i] = __builtin_fminf(lo[i], f[i]);
         hi[i] = __builtin_fmaxf(hi[i], f[i]);
       }
     }
-    block_fold(&plo, &phi);
-  }
-  if (tid < kFusedCh) {
-    float s, z;
-    params_from_range(plo, phi, s, z);
-    prm[0][tid] = s;
-    prm[1][tid] = 1.0f / s;
-    prm[2][tid] = z;
-    if (part == 0) {
-      scale[slab * kFusedCh + tid] = s;
-      zero[slab * kFusedCh + tid] = (uint8_t)z;
+#pragma unroll
+    for (int k = 0; k < R; ++k) asm volatile("" : "+v"(v[k]));
+    // the first tensor's parameters were read into registers before any thread could reach
+    // the barriers of this second exchange, so sh.prm may be rewritten
+    fused_slab_params(sh, b, lo, hi, tokens, channels, slab, part, epoch, spin_ticks);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s8[i] = sh.prm[0][lc * 8 + i];
+      r8[i] = sh.prm[1][lc * 8 + i];
+      z8[i] = sh.prm[2][lc * 8 + i];
     }
-  }
-  __syncthreads();
-
-  // ---- codes of the resident rows
-  float s8[8], r8[8], z8[8];
+    qp = b.q + (size_t)(t0 + rr) * channels + c0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s8[i] = prm[0][lc * 8 + i];
-    r8[i] = prm[1][lc * 8 + i];
-    z8[i] = prm[2][lc * 8 + i];
-  }
-  // Rows t0 + rr + 64 k, k < nk, are this thread's: one live count and one moving pointer.  (A
-  // token index per row does not fit beside the rows; a spilled one costs a wait on every row,
-  // because stores count in the same counter as the spill reload.)
-  const int nk = max(0, (t1 - t0 - rr + kFusedRowsPerPass - 1) / kFusedRowsPerPass);
-  uint8_t* qp = q + (size_t)(t0 + rr) * channels + c0;
-  const size_t pass = (size_t)kFusedRowsPerPass * channels;
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    if (k < nk) __builtin_nontemporal_store(quant_row8(v[k], s8, r8, z8), reinterpret_cast<v2u*>(qp));
-    qp += pass;
+    for (int k = 0; k < R; ++k) {
+      if (k < nk) __builtin_nontemporal_store(quant_row8(v[k], s8, r8, z8), reinterpret_cast<v2u*>(qp));
+      qp += pass;
+    }
   }
 }
 
@@ -524,17 +618,19 @@ static int fused_rows(int tokens, int channels) {
   return rows <= kFusedMaxRows ? rows : 0;
 }
 
+// One size serves both calls: the paired call's two fused regions, or the three-pass
+// schedule's partials (which the paired call's fallback uses for one tensor after the other).
 size_t kv_workspace_bytes(int tokens, int channels) {
   if (tokens <= 0 || channels <= 0) return 0;
   const size_t three_pass = (size_t)2 * kv_range_chunks(tokens) * channels * sizeof(float);
-  const size_t nslabs = (size_t)(channels / kFusedCh);
-  const size_t fused = nslabs * kFusedParts * (16 + 2 * kFusedCh * sizeof(float));
+  const size_t fused = 2 * fused_region_bytes(channels);
   return three_pass > fused ? three_pass : fused;
 }
 
-// Epoch of a fused call: strictly increasing per process, started at a time-dependent value,
-// so a tag left in a workspace by an earlier call (or by whatever the memory held before)
-// never matches the running call.
+// Epoch of a fused call: strictly increasing per process and never 0, started at a
+// time-dependent value, so a word left in a workspace by an earlier call of this process never
+// carries the running call's epoch (what the memory held before, from elsewhere, matches with
+// chance 2^-32 per word).
 static uint32_t next_epoch() {
   static std::atomic<uint32_t> counter{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
   uint32_t e = counter.fetch_add(1) + 1;
@@ -548,63 +644,81 @@ static long long spin_ticks() {
   return v ? std::atoll(v) : 10000000LL;
 }
 
-// Blocks of kv_quant_fused_kernel<8 n> that the current device holds at once (0 if unknown).
-// The exchange waits for every part of a slab, so the fused pass is launched only when the
-// whole grid is resident together; the bounded wait stays as the guard for anything else
-// sharing the device.
-static int fused_resident_blocks(int n) {
-  static const void* const fns[6] = {
-      nullptr,
-      reinterpret_cast<const void*>(&kv_quant_fused_kernel<8>),
-      reinterpret_cast<const void*>(&kv_quant_fused_kernel<16>),
-      reinterpret_cast<const void*>(&kv_quant_fused_kernel<24>),
-      reinterpret_cast<const void*>(&kv_quant_fused_kernel<32>),
-      reinterpret_cast<const void*>(&kv_quant_fused_kernel<40>)};
+template <bool kPair>
+static const void* fused_fn(int n) {
+  switch (n) {
+    case 1: return reinterpret_cast<const void*>(&kv_quant_fused_kernel<8, kPair>);
+    case 2: return reinterpret_cast<const void*>(&kv_quant_fused_kernel<16, kPair>);
+    case 3: return reinterpret_cast<const void*>(&kv_quant_fused_kernel<24, kPair>);
+    case 4: return reinterpret_cast<const void*>(&kv_quant_fused_kernel<32, kPair>);
+    case 5: return reinterpret_cast<const void*>(&kv_quant_fused_kernel<40, kPair>);
+    default: return nullptr;
+  }
+}
+
+// Blocks of kv_quant_fused_kernel<8 n, pair> that the current device holds at once (0 if
+// unknown).  The exchange waits for every part of a slab, so the fused pass is launched only
+// when the whole grid is resident together; the bounded wait stays as the guard for anything
+// else sharing the device.
+static int fused_resident_blocks(int n, bool pair) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices][6];  // value + 1; 0 = not yet queried
+  static std::atomic<int> cache[kMaxDevices][2][6];  // value + 1; 0 = not yet queried
   int dev = 0;
   if (n < 1 || n > 5 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  const int c = cache[dev][n].load(std::memory_order_relaxed);
+  const int c = cache[dev][pair][n].load(std::memory_order_relaxed);
   if (c) return c - 1;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[n], kFusedThreads, 0) != hipSuccess ||
+  const void* fn = pair ? fused_fn<true>(n) : fused_fn<false>(n);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kFusedThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     (void)hipGetLastError();  // leave no sticky error behind; use the three-pass path
     return 0;
   }
   const int blocks = per_cu * cus;
-  cache[dev][n].store(blocks + 1, std::memory_order_relaxed);
+  cache[dev][pair][n].store(blocks + 1, std::memory_order_relaxed);
   return blocks;
 }
 
-hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t* q,
-                           float* scale, uint8_t* zero, void* workspace, hipStream_t stream) {
+// Rows per thread of the fused launch for this shape, or 0 when the three-pass schedule runs.
+static int fused_choice(int tokens, int channels, bool pair) {
   const int rows = fused_rows(tokens, channels);
-  if (rows > 0 && (channels / kFusedCh) * kFusedParts <= fused_resident_blocks((rows + 7) / 8)) {
-    const int nslabs = channels / kFusedCh;
-    uint32_t* tags = reinterpret_cast<uint32_t*>(workspace);
-    float* parts = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
-                                            (size_t)nslabs * kFusedParts * 16);
-    const dim3 grid(nslabs * kFusedParts), block(kFusedThreads);
-    const uint32_t epoch = next_epoch();
-    const long long ticks = spin_ticks();
-    switch ((rows + 7) / 8) {
-#define SVDQ_KV_FUSED(n)                                                                       \
-  case n:                                                                                      \
-    hipLaunchKernelGGL(kv_quant_fused_kernel<8 * n>, grid, block, 0, stream, x, tokens,        \
-                       channels, q, scale, zero, tags, parts, epoch, ticks);                   \
+  if (rows == 0) return 0;
+  const int n = (rows + 7) / 8;
+  return (channels / kFusedCh) * kFusedParts <= fused_resident_blocks(n, pair) ? n : 0;
+}
+
+template <bool kPair>
+static hipError_t launch_fused(int n, const KvFusedTensor& a, const KvFusedTensor& b, int tokens,
+                               int channels, hipStream_t stream) {
+  const dim3 grid((channels / kFusedCh) * kFusedParts), block(kFusedThreads);
+  const uint32_t epoch = next_epoch();
+  const long long ticks = spin_ticks();
+  switch (n) {
+#define SVDQ_KV_FUSED(n)                                                                        \
+  case n:                                                                                       \
+    hipLaunchKernelGGL((kv_quant_fused_kernel<8 * n, kPair>), grid, block, 0, stream, a, b,     \
+                       tokens, channels, epoch, ticks);                                         \
     break;
-      SVDQ_KV_FUSED(1)
-      SVDQ_KV_FUSED(2)
-      SVDQ_KV_FUSED(3)
-      SVDQ_KV_FUSED(4)
-      SVDQ_KV_FUSED(5)
+    SVDQ_KV_FUSED(1)
+    SVDQ_KV_FUSED(2)
+    SVDQ_KV_FUSED(3)
+    SVDQ_KV_FUSED(4)
+    SVDQ_KV_FUSED(5)
 #undef SVDQ_KV_FUSED
-      default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    default:
+      return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+static KvFusedTensor fused_tensor(const uint16_t* x, uint8_t* q, float* scale, uint8_t* zero,
+                                  void* region) {
+  return KvFusedTensor{x, q, scale, zero, reinterpret_cast<uint64_t*>(region)};
+}
+
+static hipError_t launch_three_pass(const uint16_t* x, int tokens, int channels, uint8_t* q,
+                                    float* scale, uint8_t* zero, void* workspace,
+                                    hipStream_t stream) {
   const int nslabs = kv_slabs(channels), nchunks = kv_range_chunks(tokens);
   float* part_lo = reinterpret_cast<float*>(workspace);
   float* part_hi = part_lo + (size_t)nchunks * channels;
@@ -620,6 +734,30 @@ hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t*
   hipLaunchKernelGGL(kv_quant_kernel, grid_q, dim3(256), 0, stream, x, tokens, channels, scale,
                      zero, q);
   return hipGetLastError();
+}
+
+hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t* q,
+                           float* scale, uint8_t* zero, void* workspace, hipStream_t stream) {
+  if (const int n = fused_choice(tokens, channels, false)) {
+    const KvFusedTensor a = fused_tensor(x, q, scale, zero, workspace);
+    return launch_fused<false>(n, a, a, tokens, channels, stream);
+  }
+  return launch_three_pass(x, tokens, channels, q, scale, zero, workspace, stream);
+}
+
+hipError_t launch_kv_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                                uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv,
+                                uint8_t* zv, void* workspace, hipStream_t stream) {
+  if (const int n = fused_choice(tokens, channels, true)) {
+    const KvFusedTensor a = fused_tensor(k, qk, sk, zk, workspace);
+    const KvFusedTensor b = fused_tensor(
+        v, qv, sv, zv, reinterpret_cast<uint8_t*>(workspace) + fused_region_bytes(channels));
+    return launch_fused<true>(n, a, b, tokens, channels, stream);
+  }
+  // one tensor after the other on the stream, sharing the workspace
+  const hipError_t e = launch_kv_quant(k, tokens, channels, qk, sk, zk, workspace, stream);
+  if (e != hipSuccess) return e;
+  return launch_kv_quant(v, tokens, channels, qv, sv, zv, workspace, stream);
 }
 
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,

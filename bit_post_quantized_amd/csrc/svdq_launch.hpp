@@ -45,6 +45,10 @@ size_t kv_workspace_bytes(int tokens, int channels);
 hipError_t launch_kv_quant(const uint16_t* x, int tokens, int channels, uint8_t* q,
                            float* scale, uint8_t* zero, void* workspace, hipStream_t stream);
 
+hipError_t launch_kv_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                                uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv,
+                                uint8_t* zv, void* workspace, hipStream_t stream);
+
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,
                              int tokens, int channels, uint16_t* x_out, hipStream_t stream);
 

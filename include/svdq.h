@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 5
+#define SVDQ_ABI_VERSION 6
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -191,14 +191,15 @@ int svdq_w4a8_partials(const int8_t* xq8, const uint8_t* wq, int M, int N, int K
                        void* stream);
 
 /*
- * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant needs for the
- * cross-token min/max reduction of its per-channel ranges (VARC "INT8 KV cache quantization":
- * statistics per channel over the cached tokens; 0 when tokens == 0): the per-part partial ranges and tags of
- * the single-pass schedule, or the per-64-token-chunk partials of the three-pass schedule for
- * shapes the single pass does not take; the size covers either.  Its contents need no
- * initialization and carry nothing between calls (a tag left by an earlier call never matches
- * a later one); calls that share one workspace must not overlap in time (one stream, or one
- * workspace per stream).
+ * kv_int8_workspace_bytes — size of the caller-owned scratch that kv_int8_quant and
+ * kv_int8_quant_pair need for the cross-token min/max reduction of their per-channel ranges
+ * (VARC "INT8 KV cache quantization": statistics per channel over the cached tokens; 0 when
+ * tokens == 0): the per-part partial ranges and tags of the single-pass schedule (two tensors'
+ * worth, for the paired call), or the per-64-token-chunk partials of the three-pass schedule
+ * for shapes the single pass does not take; the size covers every case of both calls.  Its
+ * contents need no initialization and carry nothing between calls (a tag left by an earlier
+ * call never matches a later one); calls that share one workspace must not overlap in time
+ * (one stream, or one workspace per stream).
  */
 size_t kv_int8_workspace_bytes(int tokens, int channels);
 
@@ -216,6 +217,22 @@ size_t kv_int8_workspace_bytes(int tokens, int channels);
  */
 int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float* scale,
                   uint8_t* zero, void* workspace, void* stream);
+
+/*
+ * kv_int8_quant_pair — kv_int8_quant of two tensors of one shape, a layer's K and V cache
+ * (VARC "INT8 KV cache quantization": both caches are stored as per-channel INT8), in one
+ * launch: the codes, scales and zeros are those of two kv_int8_quant calls, bit for bit.  The
+ * single-pass schedule stores K's codes while it reads V, so the two tensors' traffic overlaps;
+ * shapes the single pass does not take run two kv_int8_quant calls on the stream.
+ *   k, v          bf16 [tokens, channels]                          16B
+ *   qk, qv        uint8 [tokens, channels]                         16B
+ *   sk, sv        fp32 [channels] (16B);  zk, zv  uint8 [channels] (16B)
+ *   workspace     device scratch of kv_int8_workspace_bytes(tokens, channels) bytes   16B
+ *   Limits and errors as kv_int8_quant.  No output may overlap an input or another output.
+ */
+int kv_int8_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                       uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv, uint8_t* zv,
+                       void* workspace, void* stream);
 
 /*
  * kv_int8_dequant — the inverse map of kv_int8_quant's affine code (VARC "INT8 KV cache

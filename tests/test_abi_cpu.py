@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 5
+    assert lib.svdq_abi_version() == 6
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -162,6 +162,22 @@ def test_kv_validation(lib):
     assert q(FAKE, 65535 * 32 + 1, 8, FAKE, FAKE, FAKE, FAKE, None) == binding.SVDQ_ESHAPE
     assert d(FAKE, FAKE, FAKE, 65535 * 32 + 1, 8, FAKE, None) == binding.SVDQ_ESHAPE
     assert b"2097120" in lib.svdq_last_error()
+    # small token counts: the paired single pass's two regions of published part ranges
+    # (32 slabs x 8 parts x 256 tagged 8-byte words each) exceed one 64-token chunk's partials
+    assert lib.kv_int8_workspace_bytes(64, 4096) == 2 * 32 * 8 * 256 * 8
+
+
+def test_kv_pair_validation(lib):
+    p = lib.kv_int8_quant_pair
+    f8 = [FAKE] * 8
+    assert p(FAKE, FAKE, 16, 12, *f8[:6], FAKE, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, FAKE, -1, 16, *f8[:6], FAKE, None) == binding.SVDQ_EINVAL
+    assert p(FAKE, None, 16, 16, *f8[:6], FAKE, None) == binding.SVDQ_EINVAL
+    assert p(FAKE, FAKE, 16, 16, *f8[:6], None, None) == binding.SVDQ_EINVAL
+    assert p(FAKE, FAKE, 16, 16, FAKE, FAKE, FAKE, FAKE, ODD, FAKE, FAKE, None) == \
+        binding.SVDQ_EALIGN
+    assert p(FAKE, FAKE, 65535 * 32 + 1, 8, *f8[:6], FAKE, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, FAKE, 0, 16, *f8[:6], None, None) == binding.SVDQ_OK
 
 
 def test_kv_attention_validation(lib):
