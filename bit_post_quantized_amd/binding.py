@@ -43,6 +43,7 @@ _SIGNATURES = {
     "kv_int8_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "kv_int8_quant": ([_P, _I, _I, _P, _P, _P, _P, _P], _I),
     "kv_int8_quant_pair": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "kv_int8_quant_pair_noalloc": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
     "kv_int8_dequant": ([_P, _P, _P, _I, _I, _P, _P], _I),
     "kv_int8_attention_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
     "kv_int8_attention": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P,
@@ -308,6 +309,22 @@ def kv_int8_quant_pair(k: torch.Tensor, v: torch.Tensor, qk: torch.Tensor, sk: t
             a(qv, n, "qv", _U8), a(sv, 4 * channels, "sv", _F32), a(zv, channels, "zv", _U8),
             a(workspace, kv_int8_workspace_bytes(tokens, channels) if tokens else 0, "workspace"))
     _check(fn, load().kv_int8_quant_pair(*args, a.stream(stream)))
+
+
+def kv_int8_quant_pair_noalloc(k: torch.Tensor, v: torch.Tensor, qk: torch.Tensor,
+                               sk: torch.Tensor, zk: torch.Tensor, qv: torch.Tensor,
+                               sv: torch.Tensor, zv: torch.Tensor, stream=None) -> None:
+    """kv_int8_quant_pair on the library's own device scratch (no workspace, no allocation)."""
+    fn = "kv_int8_quant_pair_noalloc"
+    tokens, channels = _kv_shape(k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"{fn}: v must have the shape of k {tuple(k.shape)}, got {tuple(v.shape)}")
+    a = _Args(fn)
+    n = tokens * channels
+    args = (a(k, 2 * n, "k", _BF16), a(v, 2 * n, "v", _BF16), tokens, channels,
+            a(qk, n, "qk", _U8), a(sk, 4 * channels, "sk", _F32), a(zk, channels, "zk", _U8),
+            a(qv, n, "qv", _U8), a(sv, 4 * channels, "sv", _F32), a(zv, channels, "zv", _U8))
+    _check(fn, load().kv_int8_quant_pair_noalloc(*args, a.stream(stream)))
 
 
 def kv_int8_dequant(q: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor,

@@ -278,6 +278,26 @@ int kv_int8_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int cha
                     "kv_int8_quant_pair");
 }
 
+int kv_int8_quant_pair_noalloc(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                               uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv,
+                               uint8_t* zv, void* stream) {
+  if (int s = check_kv(tokens, channels)) return s;
+  if (!k || !v || !qk || !sk || !zk || !qv || !sv || !zv) return fail(SVDQ_EINVAL, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(qk) || !aligned16(sk) || !aligned16(zk) ||
+      !aligned16(qv) || !aligned16(sv) || !aligned16(zv))
+    return fail(SVDQ_EALIGN, "tensors must be 16-byte aligned");
+  const size_t need = svdq::kv_workspace_bytes(tokens, channels);
+  if (need > svdq::kKvStaticScratchBytes)
+    return fail(SVDQ_ESHAPE,
+                "tokens %d x channels %d need %zu bytes of scratch; this entry point holds %zu "
+                "(use kv_int8_quant_pair with a workspace)",
+                tokens, channels, need, svdq::kKvStaticScratchBytes);
+  if (tokens == 0) return ok();
+  return hip_status(svdq::launch_kv_quant_pair_noalloc(k, v, tokens, channels, qk, sk, zk, qv, sv,
+                                                       zv, (hipStream_t)stream),
+                    "kv_int8_quant_pair_noalloc");
+}
+
 int kv_int8_dequant(const uint8_t* q, const float* scale, const uint8_t* zero, int tokens,
                     int channels, uint16_t* x_out, void* stream) {
   if (int s = check_kv(tokens, channels)) return s;

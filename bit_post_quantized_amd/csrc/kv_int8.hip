@@ -34,6 +34,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstdlib>
+#include <mutex>
 
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
@@ -758,6 +759,45 @@ hipError_t launch_kv_quant_pair(const uint16_t* k, const uint16_t* v, int tokens
   const hipError_t e = launch_kv_quant(k, tokens, channels, qk, sk, zk, workspace, stream);
   if (e != hipSuccess) return e;
   return launch_kv_quant(v, tokens, channels, qv, sv, zv, workspace, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// Device scratch of kv_int8_quant_pair_noalloc: a file-scope array that every device the library
+// runs on holds until the process ends.  Host code never passes the array's name to a kernel or
+// a copy (on the host it is only a stand-in): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.  Nothing in
+// it needs to start at zero (the single pass accepts only words tagged with the running call's
+// epoch; the three-pass schedule writes every partial before reading it); calls that overlap in
+// time on one device share it and race.
+static __device__ __align__(256) unsigned char scratch[kKvStaticScratchBytes];
+
+static hipError_t static_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_kv_quant_pair_noalloc(const uint16_t* k, const uint16_t* v, int tokens,
+                                        int channels, uint8_t* qk, float* sk, uint8_t* zk,
+                                        uint8_t* qv, float* sv, uint8_t* zv, hipStream_t stream) {
+  if (kv_workspace_bytes(tokens, channels) > kKvStaticScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_kv_quant_pair(k, v, tokens, channels, qk, sk, zk, qv, sv, zv, ws, stream);
 }
 
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,

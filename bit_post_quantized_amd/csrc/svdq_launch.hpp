@@ -49,6 +49,12 @@ hipError_t launch_kv_quant_pair(const uint16_t* k, const uint16_t* v, int tokens
                                 uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv,
                                 uint8_t* zv, void* workspace, hipStream_t stream);
 
+// scratch that kv_int8_quant_pair_noalloc holds per device (16 MiB)
+constexpr size_t kKvStaticScratchBytes = (size_t)16 << 20;
+hipError_t launch_kv_quant_pair_noalloc(const uint16_t* k, const uint16_t* v, int tokens,
+                                        int channels, uint8_t* qk, float* sk, uint8_t* zk,
+                                        uint8_t* qv, float* sv, uint8_t* zv, hipStream_t stream);
+
 hipError_t launch_kv_dequant(const uint8_t* q, const float* scale, const uint8_t* zero,
                              int tokens, int channels, uint16_t* x_out, hipStream_t stream);
 

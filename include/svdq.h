@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 6
+#define SVDQ_ABI_VERSION 7
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -233,6 +233,22 @@ int kv_int8_quant(const uint16_t* x, int tokens, int channels, uint8_t* q, float
 int kv_int8_quant_pair(const uint16_t* k, const uint16_t* v, int tokens, int channels,
                        uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv, uint8_t* zv,
                        void* workspace, void* stream);
+
+/*
+ * kv_int8_quant_pair_noalloc — kv_int8_quant_pair without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The scratch is a 16 MiB array in the
+ * library's device code, which every device the library runs on holds until the process ends;
+ * the call makes no hipMalloc, hipFree or other allocating call.  Same arguments (less
+ * workspace), results and limits as kv_int8_quant_pair, and additionally
+ * kv_int8_workspace_bytes(tokens, channels) <= 16 MiB (SVDQ_ESHAPE otherwise; e.g. 10240 tokens
+ * x 4096 channels need 5 MiB).  The scratch carries nothing between calls, but all calls on one
+ * device share it: calls that overlap in time on one device (several streams, or several host
+ * threads) race and must be serialized by the caller.
+ */
+int kv_int8_quant_pair_noalloc(const uint16_t* k, const uint16_t* v, int tokens, int channels,
+                               uint8_t* qk, float* sk, uint8_t* zk, uint8_t* qv, float* sv,
+                               uint8_t* zv, void* stream);
 
 /*
  * kv_int8_dequant — the inverse map of kv_int8_quant's affine code (VARC "INT8 KV cache

@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 6
+    assert lib.svdq_abi_version() == 7
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -178,6 +178,20 @@ def test_kv_pair_validation(lib):
         binding.SVDQ_EALIGN
     assert p(FAKE, FAKE, 65535 * 32 + 1, 8, *f8[:6], FAKE, None) == binding.SVDQ_ESHAPE
     assert p(FAKE, FAKE, 0, 16, *f8[:6], None, None) == binding.SVDQ_OK
+
+
+def test_kv_pair_noalloc_validation(lib):
+    p = lib.kv_int8_quant_pair_noalloc
+    f6 = [FAKE] * 6
+    assert p(FAKE, FAKE, 16, 12, *f6, None) == binding.SVDQ_ESHAPE
+    assert p(FAKE, None, 16, 16, *f6, None) == binding.SVDQ_EINVAL
+    assert p(FAKE, FAKE, 16, 16, FAKE, FAKE, ODD, FAKE, FAKE, FAKE, None) == binding.SVDQ_EALIGN
+    assert p(FAKE, FAKE, 0, 16, *f6, None) == binding.SVDQ_OK
+    # beyond the 16 MiB of device scratch it holds: rejected before any HIP call
+    assert lib.kv_int8_workspace_bytes(65536, 4096) > 16 << 20
+    assert p(FAKE, FAKE, 65536, 4096, *f6, None) == binding.SVDQ_ESHAPE
+    assert b"holds 16777216" in lib.svdq_last_error()
+    assert lib.kv_int8_workspace_bytes(10240, 4096) <= 16 << 20
 
 
 def test_kv_attention_validation(lib):

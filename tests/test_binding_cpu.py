@@ -87,6 +87,9 @@ def _cases():
          dict(k=([kv_t, heads, dim], bf16), v=([kv_t, heads, dim], bf16), qk=([kv_t, C], u8),
               sk=([C], f32), zk=([C], u8), qv=([kv_t, C], u8), sv=([C], f32), zv=([C], u8),
               workspace=([B.kv_int8_workspace_bytes(kv_t, C)], u8)), {}),
+        (B.kv_int8_quant_pair_noalloc, ["k", "v", "qk", "sk", "zk", "qv", "sv", "zv"],
+         dict(k=([kv_t, heads, dim], bf16), v=([kv_t, heads, dim], bf16), qk=([kv_t, C], u8),
+              sk=([C], f32), zk=([C], u8), qv=([kv_t, C], u8), sv=([C], f32), zv=([C], u8)), {}),
         (B.kv_int8_dequant, ["q", "scale", "zero", "x_out"],
          dict(q=([kv_t, C], u8), scale=([C], f32), zero=([C], u8), x_out=([kv_t, C], bf16)),
          {}),
