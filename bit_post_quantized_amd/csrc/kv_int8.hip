@@ -75,6 +75,38 @@ __device__ __forceinline__ void decode8_bf16(const v4u w, float* v) {
   v[7] = __uint_as_float(w.w & 0xFFFF0000u);
 }
 
+// Range of 8 channels folded on the raw bf16 bits, two channels per packed 16-bit max.  A
+// non-negative bf16's bits order as a signed 16-bit integer and every negative one compares
+// below them, so the signed max over a channel (from 0) is the bits of max(0, max x); a
+// negative bf16's bits order by magnitude as an unsigned 16-bit integer and compare above every
+// non-negative one, so the unsigned max (from 0) has its sign bit set exactly when the channel
+// holds a negative value, and is then the bits of min x.  (x is finite.)
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2s16, a),
+                                                                __builtin_bit_cast(v2s16, b)));
+}
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
+                                                                __builtin_bit_cast(v2u16, b)));
+}
+
+// hb, lb: the signed and unsigned packed maxima of 8 channels (channel 2j in the low half of
+// word j) -> lo = min(0, min x), hi = max(0, max x) as floats
+__device__ __forceinline__ void range_from_bits(const uint32_t* hb, const uint32_t* lb,
+                                                float* lo, float* hi) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi[2 * j] = __uint_as_float(hb[j] << 16);
+    hi[2 * j + 1] = __uint_as_float(hb[j] & 0xFFFF0000u);
+    lo[2 * j] = (lb[j] & 0x8000u) ? __uint_as_float(lb[j] << 16) : 0.0f;
+    lo[2 * j + 1] = (lb[j] & 0x80000000u) ? __uint_as_float(lb[j] & 0xFFFF0000u) : 0.0f;
+  }
+}
+
 // ---------------------------------------------------------------- workspace
 // part_lo[chunks][channels], part_hi[chunks][channels]: one partial range per 64-token chunk,
 // fully rewritten by every call (no state survives between calls).
@@ -89,7 +121,8 @@ __device__ __forceinline__ void params_from_range(float lo, float hi, float& s, 
   z = __builtin_fminf(__builtin_fmaxf(rne_quotient(-lo, s, 1.0f / s), 0.0f), 255.0f);
 }
 
-// Codes of one row of 8 channels.
+// Codes of one row of 8 channels.  rne(x / s) + z is an integer in fp32; v_cvt_pk_u8_f32
+// converts it exactly and saturates to [0, 255], which is the clamp.
 __device__ __forceinline__ v2u quant_row8(const v4u w, const float* s, const float* rcp,
                                           const float* z) {
   float v[8];
@@ -97,10 +130,9 @@ __device__ __forceinline__ v2u quant_row8(const v4u w, const float* s, const flo
   uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = rne_quotient(v[i], s[i], rcp[i]) + z[i];
-    const float b = rne_quotient(v[4 + i], s[4 + i], rcp[4 + i]) + z[4 + i];
-    w0 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(a, 0.0f, 255.0f), i, w0);
-    w1 = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(b, 0.0f, 255.0f), i, w1);
+    w0 = __builtin_amdgcn_cvt_pk_u8_f32(rne_quotient(v[i], s[i], rcp[i]) + z[i], i, w0);
+    w1 = __builtin_amdgcn_cvt_pk_u8_f32(rne_quotient(v[4 + i], s[4 + i], rcp[4 + i]) + z[4 + i],
+                                        i, w1);
   }
   return v2u{w0, w1};
 }
@@ -527,21 +559,20 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
     v[k] = __builtin_nontemporal_load(row_of(a.x, k));
     if (k >= kFusedInFlight) asm volatile("" : "+v"(v[k - kFusedInFlight])::"memory");
   }
-  // min / max of the thread's 8 channels over its rows (written out here: a helper or lambda
-  // that takes the row array by reference leaves it in scratch memory)
+  // range of the thread's 8 channels over its rows, on the raw bits (written out here: a helper
+  // or lambda that takes the row array by reference leaves it in scratch memory)
   float lo[8], hi[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0.0f;
+  uint32_t hb[4] = {0u, 0u, 0u, 0u}, lb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    float f[8];
-    decode8_bf16(v[k], f);
+    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo[i] = __builtin_fminf(lo[i], f[i]);
-      hi[i] = __builtin_fmaxf(hi[i], f[i]);
+    for (int j = 0; j < 4; ++j) {
+      hb[j] = pk_max_i16(hb[j], w[j]);
+      lb[j] = pk_max_u16(lb[j], w[j]);
     }
   }
+  range_from_bits(hb, lb, lo, hi);
   // keep only the packed rows live across the exchange (the codes decode them again)
 #pragma unroll
   for (int k = 0; k < R; ++k) asm volatile("" : "+v"(v[k]));
@@ -580,17 +611,17 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
       if (k >= kPairInFlight) asm volatile("" : "+v"(v[k - kPairInFlight])::"memory");
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0.0f;
+    for (int j = 0; j < 4; ++j) hb[j] = lb[j] = 0u;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      float f[8];
-      decode8_bf16(v[k], f);
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = __builtin_fminf(lo[i], f[i]);
-        hi[i] = __builtin_fmaxf(hi[i], f[i]);
+      for (int j = 0; j < 4; ++j) {
+        hb[j] = pk_max_i16(hb[j], w[j]);
+        lb[j] = pk_max_u16(lb[j], w[j]);
       }
     }
+    range_from_bits(hb, lb, lo, hi);
 #pragma unroll
     for (int k = 0; k < R; ++k) asm volatile("" : "+v"(v[k]));
     // the first tensor's parameters were read into registers before any thread could reach
