@@ -31,17 +31,24 @@
 
 namespace svdq {
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int v6u __attribute__((ext_vector_type(6)));
+
 constexpr int kActRows = 16;    // tokens per workgroup
 // Waves per workgroup and groups per wave whose code loads are in flight together, by the
 // rank's 16-wide tiles NTR.  Eight waves share a workgroup's groups.  Up to rank 32 they stay
 // within 128 VGPRs, so two workgroups share a CU and a 4608-row pass (288 workgroups) is
 // resident at once: 16 waves per workgroup (one workgroup per CU, 256 in a first round and 32
-// in a second) took 23.2 against 20.9 us inside the bench step.  At K = 3072 each wave takes
-// two batches of 3 groups.  Larger ranks (LoRA adapters) hold more low-rank operands and
-// accumulators (<= 256 VGPRs): batches of 6 groups, and from rank 96 on, batches of 3 (no
-// spills at any rank).
+// in a second) took 23.2 against 20.9 us inside the bench step.  A wave keeps a batch of
+// groups in flight and refills each slot with the next batch's group once it has been read:
+// 3 groups for the nibble and int8 containers, 2 for BF6 (whose conversion needs 16 more
+// registers).  Larger ranks (LoRA adapters) hold more low-rank operands and accumulators
+// (<= 256 VGPRs): batches of 6 groups, and from rank 96 on, batches of 3 (no spills at any
+// rank).
 constexpr int act_max_waves(int) { return 8; }
-constexpr int act_batch(int ntr) { return ntr <= 2 || ntr >= 6 ? 3 : 6; }
+constexpr int act_batch(int ntr, int codes) {
+  return codes == kCodesBf6 && ntr <= 2 ? 2 : ntr <= 2 || ntr >= 6 ? 3 : 6;
+}
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
 // max over the four lanes of a quad (one row): DPP quad permutations [1, 0, 3, 2] and
@@ -85,6 +92,21 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   float* lam = smem;
   float* red = smem + (LAM_LDS ? K : 0);
 
+  constexpr int kActBatch = act_batch(NTR, CODES);
+  // Rolling pipeline over the wave's groups j0 + b nwaves: slot b of raw holds the activations
+  // of the batch's group b, and is refilled with group b of the next batch as soon as it has
+  // been read, so the next batch's loads are in flight under this batch's work (group index
+  // clamped; a clamped duplicate is computed but neither stored nor accumulated).  The first
+  // batch is requested before inv_lambda is staged, so the two round trips overlap.
+  v4u raw[kActBatch][2];
+#pragma unroll
+  for (int b = 0; b < kActBatch; ++b) {
+    const int g = min(wave + b * nwaves, G - 1);
+    const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
+    raw[b][0] = p[0];
+    raw[b][1] = p[1];
+  }
+
   // inv_lambda is shared by every row: one coalesced copy into LDS per workgroup, so the group
   // loop's only global loads are the activations and L1, and no wait on them also waits for
   // the code stores (which count in the same counter)
@@ -111,26 +133,18 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
     }
   };
 
-  constexpr int kActBatch = act_batch(NTR);
+  // L1 operands, one group ahead of their use along the wave's whole sequence of groups (the
+  // next batch's first group is requested under this batch's last)
+  v4u bfr[2][NT][2];
+  load_l1(min(wave, G - 1), bfr[0]);
   for (int j0 = wave; j0 < G; j0 += kActBatch * nwaves) {
-    // every load of the batch is issued before any of it is used (group index clamped; a
-    // clamped duplicate is computed but neither stored nor accumulated)
-    v4u raw[kActBatch][2];
-#pragma unroll
-    for (int b = 0; b < kActBatch; ++b) {
-      const int g = min(j0 + b * nwaves, G - 1);
-      const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
-      raw[b][0] = p[0];
-      raw[b][1] = p[1];
-    }
-    v4u bfr[2][NT][2];  // L1 operands, one group ahead
-    load_l1(min(j0, G - 1), bfr[0]);
+    const bool more = j0 + kActBatch * nwaves < G;  // uniform: this wave has a next batch
 #pragma unroll
     for (int b = 0; b < kActBatch; ++b) {
       const int g_raw = j0 + b * nwaves;
       const bool gv = g_raw < G;  // uniform over the wave
       const int g = gv ? g_raw : G - 1;
-      if (b + 1 < kActBatch) load_l1(min(j0 + (b + 1) * nwaves, G - 1), bfr[(b + 1) & 1]);
+      if (b + 1 < kActBatch || more) load_l1(min(j0 + (b + 1) * nwaves, G - 1), bfr[(b + 1) & 1]);
       const int k0 = g * kGroup + 16 * q;
       v4f l0, l1, l2, l3;
       if constexpr (LAM_LDS) {
@@ -160,6 +174,12 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
         xh[14] = __uint_as_float(w1.w << 16) * l3.z;
         xh[15] = __uint_as_float(w1.w & 0xFFFF0000u) * l3.w;
       }
+      if (more) {  // refill slot b with group b of the next batch
+        const int gn = min(j0 + (kActBatch + b) * nwaves, G - 1);
+        const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)gn * kGroup);
+        raw[b][0] = p[0];
+        raw[b][1] = p[1];
+      }
 
       // ---- group max over the row's four quarter lanes, scale, codes
       float amax = 0.0f;
@@ -177,19 +197,45 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
       // bias, clamp to [0, 15] ([0, 255]); a -0 quotient becomes the bias, so both zeros give 0
       constexpr float kBias = I8 ? 128.0f : 8.0f, kTop = I8 ? 255.0f : 15.0f;
       uint32_t bq[4];
+      if constexpr (CODES == kCodesBf6) {
+        // BF6 container: the codes as floats (-0 made +0, clamped to [-8, 7]) go through the
+        // hardware fp32 -> BF6 conversion, which packs 2 x 16 values with value 2i from the
+        // first source and 2i + 1 from the second, 6 bits each: the even and odd codes of the
+        // group give its 16 codes in order in the first three dwords (every integer in
+        // [-8, 7] is an exact E3M2 value, so the conversion only re-encodes).
+        // (elements 8..15 of each source are left undefined: they only feed output dwords 3..5,
+        // which are not stored)
+        v16f ce, co;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float v[4];
+        for (int i = 0; i < 8; ++i) {
+          ce[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[2 * i], s1, rcp) + 0.0f, -8.0f, 7.0f);
+          co[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[2 * i + 1], s1, rcp) + 0.0f, -8.0f, 7.0f);
+        }
+        // The conversion writes its first result dword before it has read every source
+        // element, and the compiler's builtin may give it a destination that overlaps a source
+        // (seen: destination v[6:11] over the first source's element 4, which then read back
+        // as the result's first dword).  So it is issued here with an early-clobber
+        // destination, disjoint from both sources, and followed by wait states before any use
+        // of its result.
+        v6u w6;
+        asm("v_cvt_scalef32_2xpk16_bf6_f32 %0, %1, %2, 1.0\n\ts_nop 7"
+                     : "=&v"(w6)
+                     : "v"(ce), "v"(co));
+        if (gv) {  // rows up to the block boundary (padding rows: zero codes)
+          uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
+          *reinterpret_cast<v3u*>(dst) = v3u{w6[0], w6[1], w6[2]};
+        }
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[4 * d + i], s1, rcp) + kBias, 0.0f, kTop);
-        bq[d] = bytes4(v);
+        for (int d = 0; d < 4; ++d) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_fmed3f(rne_quotient(xh[4 * d + i], s1, rcp) + kBias, 0.0f, kTop);
+          bq[d] = bytes4(v);
+        }
       }
       if (gv) {
-        if constexpr (CODES == kCodesBf6) {  // rows up to the block boundary (padding rows: zero codes)
-          uint8_t* dst = xq + ((size_t)(row >> 5) * G + g) * kE3m2Block + ((row & 31) + 32 * (q >> 1)) * 24 + 12 * (q & 1);
-          *reinterpret_cast<v3u*>(dst) = pack16_bf6_biased(bq);
-        }
         if (live) {
           if constexpr (CODES == kCodesNibbles)
             *reinterpret_cast<v2u*>(xq + (size_t)row * (K / 2) + (size_t)g * 32 + 8 * q) = v2u{nibbles8_biased(bq[0], bq[1]), nibbles8_biased(bq[2], bq[3])};
@@ -212,6 +258,14 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
         }
+      }
+    }
+    // an odd batch leaves the next batch's first operands in slot 1; group 0 reads slot 0
+    if constexpr (kActBatch % 2 == 1 && NTR > 0) {
+#pragma unroll
+      for (int t = 0; t < NTR; ++t) {
+        bfr[0][t][0] = bfr[1][t][0];
+        bfr[0][t][1] = bfr[1][t][1];
       }
     }
   }
