@@ -147,7 +147,7 @@ static int check_gemm(const uint8_t* xq, const uint8_t* wq, int M, int N, int K)
   if (int s = check_k(K)) return s;
   if ((long long)M * N > kMaxElems || (long long)M * K > kMaxElems || (long long)N * K > kMaxElems)
     return fail(SVDQ_ESHAPE, "problem too large");
-  if ((M + 127) / 128 > 65535) return fail(SVDQ_ESHAPE, "M too large for one launch");
+  if (M > 65535 * 128) return fail(SVDQ_ESHAPE, "M too large for one launch");
   // row offsets inside an output tile (< 256 N) are 32-bit in the kernels
   if (N > (1 << 24)) return fail(SVDQ_ESHAPE, "N must be <= 2^24 (got %d)", N);
   if (K / 64 > 65535) return fail(SVDQ_ESHAPE, "K / 64 must be <= 65535 (got K = %d)", K);
@@ -199,7 +199,7 @@ int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
 
 size_t svdq_e3m2_bytes(int rows, int K) {
   if (rows <= 0 || K <= 0 || K % 64 != 0) return 0;
-  return (size_t)((rows + 31) / 32) * (size_t)(K / 64) * (64 * 24);
+  return (((size_t)rows + 31) / 32) * (size_t)(K / 64) * (64 * 24);
 }
 
 int svdq_w4a4_gemm_e3m2(const uint8_t* xq6, const uint16_t* x_scales, const float* T,
@@ -322,8 +322,9 @@ int kv_int8_attention(const uint16_t* q, const uint8_t* k_codes, const float* k_
     return fail(SVDQ_EINVAL, "nq, tokens and heads must be positive (got %d, %d, %d)", nq, tokens,
                 heads);
   if (dim != 64 && dim != 128) return fail(SVDQ_ESHAPE, "dim must be 64 or 128 (got %d)", dim);
-  if ((long long)tokens * heads * dim > kMaxElems || nq > 65535 || heads > 65535 ||
-      (tokens + 255) / 256 > 4096)
+  // (each bound is checked before a product that could overflow uses it)
+  if (nq > 65535 || heads > 65535 || tokens > 4096 * 256 ||
+      (long long)tokens * heads * dim > kMaxElems)
     return fail(SVDQ_ESHAPE, "problem too large (at most 1048576 tokens)");
   if (!q || !k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero || !out ||
       !workspace)

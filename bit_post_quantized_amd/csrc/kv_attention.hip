@@ -24,7 +24,9 @@ namespace svdq {
 constexpr int kAttnChunk = 256;    // tokens per workgroup
 constexpr int kAttnThreads = 256;
 
-__host__ __device__ inline int attn_chunks(int tokens) { return (tokens + kAttnChunk - 1) / kAttnChunk; }
+__host__ __device__ inline int attn_chunks(int tokens) {
+  return (int)(((long long)tokens + kAttnChunk - 1) / kAttnChunk);
+}
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void kv_attn_partial_kernel(
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kCombineThreads) void kv_attn_combine_kernel(
 
 size_t kv_attn_workspace_bytes(int nq, int tokens, int heads, int dim) {
   if (nq <= 0 || tokens <= 0 || heads <= 0 || dim <= 0) return 0;
-  return (size_t)nq * heads * attn_chunks(tokens) * (dim + 2) * sizeof(float);
+  return (size_t)nq * heads * attn_chunks(tokens) * ((size_t)dim + 2) * sizeof(float);
 }
 
 hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kq, const float* ks,

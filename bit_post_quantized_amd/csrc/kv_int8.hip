@@ -110,9 +110,12 @@ __device__ __forceinline__ void range_from_bits(const uint32_t* hb, const uint32
 // ---------------------------------------------------------------- workspace
 // part_lo[chunks][channels], part_hi[chunks][channels]: one partial range per 64-token chunk,
 // fully rewritten by every call (no state survives between calls).
-__host__ __device__ inline int kv_slabs(int channels) { return (channels + kKvSlab - 1) / kKvSlab; }
+// (counts of a positive int, rounded up, in 64-bit arithmetic so no int overflows)
+__host__ __device__ inline int kv_slabs(int channels) {
+  return (int)(((long long)channels + kKvSlab - 1) / kKvSlab);
+}
 __host__ __device__ inline int kv_range_chunks(int tokens) {
-  return (tokens + kRangeTokPerBlock - 1) / kRangeTokPerBlock;
+  return (int)(((long long)tokens + kRangeTokPerBlock - 1) / kRangeTokPerBlock);
 }
 
 __device__ __forceinline__ void params_from_range(float lo, float hi, float& s, float& z) {
@@ -645,9 +648,9 @@ __global__ __launch_bounds__(kFusedThreads) void kv_quant_fused_kernel(
 // ---------------------------------------------------------------- host side
 static int fused_rows(int tokens, int channels) {
   if (channels % kFusedCh != 0 || tokens <= 0) return 0;
-  const int per = (tokens + kFusedParts - 1) / kFusedParts;
-  const int rows = (per + kFusedRowsPerPass - 1) / kFusedRowsPerPass;
-  return rows <= kFusedMaxRows ? rows : 0;
+  const long long per = ((long long)tokens + kFusedParts - 1) / kFusedParts;
+  const long long rows = (per + kFusedRowsPerPass - 1) / kFusedRowsPerPass;
+  return rows <= kFusedMaxRows ? (int)rows : 0;
 }
 
 // One size serves both calls: the paired call's two fused regions, or the three-pass

@@ -214,3 +214,42 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         binding.load(str(tmp_path / "missing.so"))
+
+
+def test_validation_paths_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """abi.cpp built for the host with AddressSanitizer and UndefinedBehaviorSanitizer and
+    linked with the library's kernel objects; tests/abi_sanitize_main.cpp calls every entry
+    point with invalid, misaligned, out-of-range and overflowing arguments (no call reaches a
+    kernel launch, so no GPU is needed) and checks the statuses; any sanitizer report fails."""
+    import glob
+    import shutil
+    import subprocess
+
+    from bit_post_quantized_amd import build
+
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no g++")
+    objs = sorted(o for o in glob.glob(os.path.join(build.OBJDIR, "*.o"))
+                  if os.path.basename(o) not in ("abi.o", "peaks.o"))
+    if not objs:
+        pytest.fail("kernel objects are not built (run python -m bit_post_quantized_amd.build)")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    sanitize = ["-fsanitize=" + "address,undefined", "-fno-sanitize-recover=all",
+                "-fno-omit-frame-pointer"]
+    common = ["-std=c++17", "-O1", "-g", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+              f"-I{os.path.join(ROOT, 'include')}", f"-I{build.CSRC}", *sanitize]
+    abi_o, main_o, exe = (str(tmp_path / n) for n in ("abi.o", "main.o", "abi_check"))
+    for src, obj in ((os.path.join(build.CSRC, "abi.cpp"), abi_o),
+                     (os.path.join(ROOT, "tests", "abi_sanitize_main.cpp"), main_o)):
+        res = subprocess.run([gxx, *common, "-c", src, "-o", obj], capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-3000:]
+    res = subprocess.run([gxx, *sanitize, main_o, abi_o, *objs, f"-L{rocm}/lib", "-lamdhip64",
+                          f"-Wl,-rpath,{rocm}/lib", "-o", exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    report = run.stdout + run.stderr
+    assert run.returncode == 0, report[-3000:]
+    assert "runtime error" not in report and "AddressSanitizer" not in report, report[-3000:]
+    assert "all ABI validation checks passed" in run.stdout
