@@ -233,7 +233,7 @@ class Peaks:
         lib.peaks_mfma_out_floats.argtypes = [ctypes.c_int]
         lib.peaks_mfma_out_floats.restype = ctypes.c_size_t
         lib.peaks_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                   ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_void_p]
         self.lib, self.torch, self.stream = lib, torch, stream
 
     def _time(self, fn, reps=5):
@@ -261,7 +261,7 @@ class Peaks:
         ms = self._time(run)
         return self.lib.peaks_mfma_flops(kind, blocks, iters) / (ms * 1e-3) / 1e12  # T/s
 
-    def copy(self, mb=1024, blocks=4096):
+    def copy(self, mode, blocks=0, mb=1024):
         torch = self.torch
         n = mb * 1024 * 1024
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
@@ -270,7 +270,7 @@ class Peaks:
 
         def run():
             if self.lib.peaks_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                   n, blocks, s) != 0:
+                                   n, mode, blocks, s) != 0:
                 raise RuntimeError("peaks_copy failed")
         ms = self._time(run)
         ok = bool(torch.equal(src[:: 1 << 16], dst[:: 1 << 16]))
@@ -512,15 +512,14 @@ def main():
         fp6 = pk.mfma(0)
         int8 = pk.mfma(1)
         bf = pk.mfma(2)
-        copies = [pk.copy(blocks=b) for b in (0, 2048, 8192)]
-        copy_gbps = max(c[0] for c in copies)
-        copy_ok = all(c[1] for c in copies)
+        shapes = {"runs_16KiB": (1, 0), "runs_64KiB": (2, 0), "stride_8192": (0, 8192)}
+        copies = {k: pk.copy(*v) for k, v in shapes.items()}
+        copy_gbps = max(c[0] for c in copies.values())
+        copy_ok = all(c[1] for c in copies.values())
         extras["measured_peaks"] = {
             "fp6_TFLOPs": round(fp6, 1), "int8_TOPS": round(int8, 1), "bf16_TFLOPs": round(bf, 1),
             "hbm_copy_GBps": round(copy_gbps, 1), "copy_verified": copy_ok,
-            "hbm_copy_GBps_by_launch": {"runs_64KiB": round(copies[0][0], 1),
-                                        "stride_2048": round(copies[1][0], 1),
-                                        "stride_8192": round(copies[2][0], 1)},
+            "hbm_copy_GBps_by_launch": {k: round(c[0], 1) for k, c in copies.items()},
             "note": "MFMA issue loops (8 independent 32x32 MFMAs per wave, 4096 workgroups of "
                     "256) and a 1 GiB device copy (best of three launch shapes); "
                     "libsvdq_peaks.so"}

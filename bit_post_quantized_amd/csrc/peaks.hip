@@ -7,8 +7,8 @@
 //    lane-dependent values fixed for the whole loop: only the matrix pipe's issue rate is
 //    measured, with no memory traffic.
 //  * peaks_copy: a device-to-device copy with 16-byte non-temporal loads and stores (grid-stride
-//    over a given grid, or one workgroup per contiguous 64 KiB run), the plain HBM stream (read +
-//    write bytes).
+//    over a given grid, or one workgroup per contiguous 16 KiB or 64 KiB run), the plain HBM
+//    stream (read + write bytes).
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -105,23 +105,31 @@ __global__ __launch_bounds__(kThreads) void copy_stream(const pk_v4u* __restrict
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// one block copies a contiguous run of kThreads * kCopyRun 16-byte vectors, every load in flight
+// one block copies a contiguous run of kThreads * RUN 16-byte vectors, every load in flight
 // before its stores
-constexpr int kCopyRun = 16;
+template <int RUN>
 __global__ __launch_bounds__(kThreads) void copy_runs(const pk_v4u* __restrict__ src,
                                                       pk_v4u* __restrict__ dst, size_t n) {
-  const size_t base = (size_t)blockIdx.x * kThreads * kCopyRun + threadIdx.x;
-  pk_v4u v[kCopyRun];
+  const size_t base = (size_t)blockIdx.x * kThreads * RUN + threadIdx.x;
+  pk_v4u v[RUN];
 #pragma unroll
-  for (int k = 0; k < kCopyRun; ++k) {
+  for (int k = 0; k < RUN; ++k) {
     const size_t i = base + (size_t)k * kThreads;
     if (i < n) v[k] = __builtin_nontemporal_load(src + i);
   }
 #pragma unroll
-  for (int k = 0; k < kCopyRun; ++k) {
+  for (int k = 0; k < RUN; ++k) {
     const size_t i = base + (size_t)k * kThreads;
     if (i < n) __builtin_nontemporal_store(v[k], dst + i);
   }
+}
+
+template <int RUN>
+static hipError_t launch_runs(const pk_v4u* s, pk_v4u* d, size_t n, hipStream_t stream) {
+  const size_t runs = (n + (size_t)kThreads * RUN - 1) / ((size_t)kThreads * RUN);
+  if (runs > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_runs<RUN>, dim3((unsigned)runs), dim3(kThreads), 0, stream, s, d, n);
+  return hipGetLastError();
 }
 
 double flops_per_mfma(int kind) {
@@ -165,22 +173,30 @@ int peaks_mfma(int kind, int blocks, int iters, float* out, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-int peaks_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
-  if (!src || !dst || bytes == 0 || bytes % 16 != 0 || blocks < 0 || blocks > 1 << 20) return 1;
+int peaks_copy(const void* src, void* dst, size_t bytes, int mode, int blocks, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16 != 0) return 1;
   if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return 3;
   const size_t n = bytes / 16;
   const auto* s = reinterpret_cast<const pk_v4u*>(src);
   auto* d = reinterpret_cast<pk_v4u*>(dst);
-  if (blocks == 0) {
-    const size_t runs = (n + (size_t)kThreads * kCopyRun - 1) / ((size_t)kThreads * kCopyRun);
-    if (runs > 0x7fffffffu) return 1;
-    hipLaunchKernelGGL(copy_runs, dim3((unsigned)runs), dim3(kThreads), 0, (hipStream_t)stream,
-                       s, d, n);
-  } else {
-    hipLaunchKernelGGL(copy_stream, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, s, d,
-                       n);
+  hipError_t e;
+  switch (mode) {
+    case PEAKS_COPY_STRIDE:
+      if (blocks <= 0 || blocks > 1 << 20) return 1;
+      hipLaunchKernelGGL(copy_stream, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, s, d,
+                         n);
+      e = hipGetLastError();
+      break;
+    case PEAKS_COPY_RUNS_16K:
+      e = launch_runs<4>(s, d, n, (hipStream_t)stream);
+      break;
+    case PEAKS_COPY_RUNS_64K:
+      e = launch_runs<16>(s, d, n, (hipStream_t)stream);
+      break;
+    default:
+      return 1;
   }
-  return hipGetLastError() == hipSuccess ? 0 : 4;
+  return e == hipSuccess ? 0 : 4;
 }
 
 }  // extern "C"

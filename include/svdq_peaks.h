@@ -35,12 +35,15 @@ size_t peaks_mfma_out_floats(int blocks);
 
 /*
  * peaks_copy — dst[0, bytes) = src[0, bytes) with 16-byte non-temporal loads and stores over
- * workgroups of 256 threads: `blocks` of them striding over the range (4 loads in flight per
- * thread), or for blocks == 0 one workgroup per contiguous 64 KiB run (16 loads in flight per
- * thread).  bytes % 16 == 0, both pointers 16-byte aligned, the ranges disjoint,
- * 0 <= blocks <= 2^20.
+ * workgroups of 256 threads, by launch shape `mode`:
+ *   PEAKS_COPY_STRIDE    `blocks` workgroups striding over the range, 4 loads in flight per
+ *                        thread (1 <= blocks <= 2^20);
+ *   PEAKS_COPY_RUNS_16K  one workgroup per contiguous 16 KiB run (4 loads per thread);
+ *   PEAKS_COPY_RUNS_64K  one workgroup per contiguous 64 KiB run (16 loads per thread).
+ * bytes % 16 == 0, both pointers 16-byte aligned, the ranges disjoint.
  */
-int peaks_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
+enum peaks_copy_mode { PEAKS_COPY_STRIDE = 0, PEAKS_COPY_RUNS_16K = 1, PEAKS_COPY_RUNS_64K = 2 };
+int peaks_copy(const void* src, void* dst, size_t bytes, int mode, int blocks, void* stream);
 
 #ifdef __cplusplus
 }
