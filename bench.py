@@ -339,7 +339,7 @@ def main():
             ("act", lambda: B.svdq_quantize_act_e3m2(X[b], pw.inv_lambda, pw.L1p, RANK, a.xq,
                                                      a.x_scales, a.T, stream)),
             ("gemm", lambda: B.svdq_w4a4_gemm_e3m2(a.xq, a.x_scales, a.T, pw.wq, pw.w_scales,
-                                                   pw.L2, None, RANK, Y[b], stream)),
+                                                   pw.L2p, None, RANK, Y[b], stream)),
             ("kv_pair", lambda: B.kv_int8_quant_pair(kvs[b][0], kvs[b][1], q[b][0], sc[b][0],
                                                      zp[b][0], q[b][1], sc[b][1], zp[b][1], wsp,
                                                      stream)),
@@ -434,11 +434,11 @@ def main():
         T4 = torch.empty(M, RANK, dtype=torch.float32, device=dev)
         xq8 = torch.empty(M, K, dtype=torch.int8, device=dev)
         extras["int8_route"] = route(
-            time10(lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2, None, RANK, Y[0], stream)),
+            time10(lambda: B.svdq_w4a4_gemm(xq4, xs4, T4, wq4, ws4, pw.L2p, None, RANK, Y[0], stream)),
             time10(lambda: B.svdq_quantize_act(X[0], pw.inv_lambda, pw.L1p, RANK, xq4, xs4, T4,
                                                stream)))
         extras["w4a8_route"] = route(
-            time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2, None, RANK, Y[0], stream)),
+            time10(lambda: B.svdq_w4a8_gemm(xq8, xs4, T4, wq4, ws4, pw.L2p, None, RANK, Y[0], stream)),
             time10(lambda: B.svdq_quantize_act_a8(X[0], pw.inv_lambda, pw.L1p, RANK, xq8, xs4, T4,
                                                   stream)))
         del wq4, ws4, xq4, xs4, T4, xq8
@@ -449,7 +449,7 @@ def main():
         al = layer.alloc_act(M, K, pwl.rank, dev, e3m2=True)
         extras["lora_route"] = route(
             time10(lambda: B.svdq_w4a4_gemm_e3m2(al.xq, al.x_scales, al.T, pwl.wq, pwl.w_scales,
-                                                 pwl.L2, None, pwl.rank, Y[0], stream)),
+                                                 pwl.L2p, None, pwl.rank, Y[0], stream)),
             time10(lambda: B.svdq_quantize_act_e3m2(X[0], pwl.inv_lambda, pwl.L1p, pwl.rank,
                                                     al.xq, al.x_scales, al.T, stream)),
             rank=RANK + LORA_RANK, adapter_rank=LORA_RANK)
@@ -488,7 +488,8 @@ def main():
             B.svdq_pack_weights_e3m2(R, wq6, ws6)
             del R
             L1p = (torch.randn(RANK, K_, generator=g, device=dev) * 0.05).to(torch.bfloat16)
-            L2s = (torch.randn(RANK, N_, generator=g, device=dev) * 0.05).to(torch.bfloat16)
+            L2s = layer.pack_lowrank_up(
+                (torch.randn(RANK, N_, generator=g, device=dev) * 0.05).to(torch.bfloat16))
             inv = torch.ones(K_, dtype=torch.float32, device=dev)
             a_s = layer.alloc_act(M_, K_, RANK, dev, e3m2=True)
             Ys = torch.empty(M_, N_, dtype=torch.bfloat16, device=dev)

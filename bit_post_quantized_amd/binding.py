@@ -29,6 +29,7 @@ _SIGNATURES = {
     "svdq_last_error": ([], ctypes.c_char_p),
     "svdq_pack_weights": ([_P, _I, _I, _P, _P, _P], _I),
     "svdq_pack_lowrank": ([_P, _I, _I, _P, _P], _I),
+    "svdq_pack_lowrank_up": ([_P, _I, _I, _P, _P], _I),
     "svdq_quantize_act": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "svdq_w4a4_gemm": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "svdq_w4a4_partials": ([_P, _P, _I, _I, _I, _P, _P], _I),
@@ -163,6 +164,15 @@ def svdq_pack_lowrank(L1: torch.Tensor, L1p: torch.Tensor, stream=None) -> None:
     _check(fn, load().svdq_pack_lowrank(*args, a.stream(stream)))
 
 
+def svdq_pack_lowrank_up(L2: torch.Tensor, L2p: torch.Tensor, stream=None) -> None:
+    """L2 bf16 [r, N] -> L2p bf16 [N, r], the GEMM epilogue's layout of the factor."""
+    fn = "svdq_pack_lowrank_up"
+    r, N = L2.shape
+    a = _Args(fn)
+    args = (a(L2, 2 * r * N, "L2", _BF16, (r, N)), r, N, a(L2p, 2 * N * r, "L2p", _BF16, (N, r)))
+    _check(fn, load().svdq_pack_lowrank_up(*args, a.stream(stream)))
+
+
 def svdq_quantize_act(X: torch.Tensor, inv_lambda: torch.Tensor, L1p: Optional[torch.Tensor],
                       r: int, xq: torch.Tensor, x_scales: torch.Tensor,
                       T: Optional[torch.Tensor], stream=None) -> None:
@@ -184,7 +194,7 @@ def _quantize_act(fn, X, inv_lambda, L1p, r, codes, code_name, code_bytes, x_sca
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
 
-def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L2, bias, M, N,
+def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L2p, bias, M, N,
           K, r, Y, stream) -> None:
     out = _out_dtype(fn, Y)
     a = _Args(fn)
@@ -192,7 +202,7 @@ def _gemm(fn, xq, x_name, x_bytes, x_scales, T, wq, w_name, w_bytes, w_scales, L
     args = (a(xq, x_bytes, x_name, _I8 if x_name == "xq8" else _U8),
             a(x_scales, 2 * G * M, "x_scales", _F16, (M, G)), a(T, 4 * M * r, "T", _F32, (M, r)),
             a(wq, w_bytes, w_name, _U8), a(w_scales, 2 * G * N, "w_scales", _F16, (G, N)),
-            a(L2, 2 * r * N, "L2", _BF16, (r, N)), a(bias, 2 * N, "bias", _BF16, (N,)),
+            a(L2p, 2 * N * r, "L2p", _BF16, (N, r)), a(bias, 2 * N, "bias", _BF16, (N,)),
             M, N, K, r, a(Y, Y.element_size() * M * N, "Y", None, (M, N)), out)
     _check(fn, getattr(load(), fn)(*args, a.stream(stream)))
 
@@ -206,13 +216,13 @@ def _partials(fn, xq, x_name, x_bytes, wq, w_name, w_bytes, M, N, K, P, stream) 
 
 
 def svdq_w4a4_gemm(xq: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
-                   wq: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
+                   wq: torch.Tensor, w_scales: torch.Tensor, L2p: Optional[torch.Tensor],
                    bias: Optional[torch.Tensor], r: int, Y: torch.Tensor, stream=None) -> None:
     """Y [M, N] (bf16 or fp32, chosen by Y's dtype) of the fused W4A4 + low-rank GEMM."""
     M, half_k = xq.shape
     N = wq.shape[0]
     _gemm("svdq_w4a4_gemm", xq, "xq", M * half_k, x_scales, T, wq, "wq", N * half_k, w_scales,
-          L2, bias, M, N, 2 * half_k, r, Y, stream)
+          L2p, bias, M, N, 2 * half_k, r, Y, stream)
 
 
 def svdq_w4a4_partials(xq: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,
@@ -250,7 +260,7 @@ def svdq_quantize_act_e3m2(X: torch.Tensor, inv_lambda: torch.Tensor,
 
 
 def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
-                        wq6: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
+                        wq6: torch.Tensor, w_scales: torch.Tensor, L2p: Optional[torch.Tensor],
                         bias: Optional[torch.Tensor], r: int, Y: torch.Tensor,
                         stream=None) -> None:
     """As svdq_w4a4_gemm, reading the BF6 containers (M, N from Y [M, N], K from
@@ -259,7 +269,7 @@ def svdq_w4a4_gemm_e3m2(xq6: torch.Tensor, x_scales: torch.Tensor, T: Optional[t
     G = w_scales.shape[0]
     K = 64 * G
     _gemm("svdq_w4a4_gemm_e3m2", xq6, "xq6", _e3m2_bytes(M, K), x_scales, T, wq6, "wq6",
-          _e3m2_bytes(N, K), w_scales, L2, bias, M, N, K, r, Y, stream)
+          _e3m2_bytes(N, K), w_scales, L2p, bias, M, N, K, r, Y, stream)
 
 
 def svdq_w4a4_partials_e3m2(xq6: torch.Tensor, wq6: torch.Tensor, M: int, N: int, K: int,
@@ -349,13 +359,13 @@ def svdq_quantize_act_a8(X: torch.Tensor, inv_lambda: torch.Tensor, L1p: Optiona
 
 
 def svdq_w4a8_gemm(xq8: torch.Tensor, x_scales: torch.Tensor, T: Optional[torch.Tensor],
-                   wq: torch.Tensor, w_scales: torch.Tensor, L2: Optional[torch.Tensor],
+                   wq: torch.Tensor, w_scales: torch.Tensor, L2p: Optional[torch.Tensor],
                    bias: Optional[torch.Tensor], r: int, Y: torch.Tensor, stream=None) -> None:
     """Y [M, N] of the W4A8 GEMM: int8 activation codes xq8 [M, K], INT4 nibbles wq [N, K/2]."""
     M, K = xq8.shape
     N = wq.shape[0]
     _gemm("svdq_w4a8_gemm", xq8, "xq8", M * K, x_scales, T, wq, "wq", N * (K // 2), w_scales,
-          L2, bias, M, N, K, r, Y, stream)
+          L2p, bias, M, N, K, r, Y, stream)
 
 
 def svdq_w4a8_partials(xq8: torch.Tensor, wq: torch.Tensor, P: torch.Tensor,

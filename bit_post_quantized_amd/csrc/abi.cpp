@@ -105,6 +105,16 @@ int svdq_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p, void* str
                     "svdq_pack_lowrank");
 }
 
+int svdq_pack_lowrank_up(const uint16_t* L2, int r, int N, uint16_t* L2p, void* stream) {
+  if (int s = check_rank(r)) return s;
+  if (r == 0) return fail(SVDQ_ESHAPE, "r must be positive for the factor relayout");
+  if (N <= 0) return fail(SVDQ_EINVAL, "N must be positive (got %d)", N);
+  if (N > (1 << 24)) return fail(SVDQ_ESHAPE, "N must be <= 2^24 (got %d)", N);
+  if (!L2 || !L2p) return fail(SVDQ_EINVAL, "NULL pointer");
+  return hip_status(svdq::launch_pack_lowrank_up(L2, r, N, L2p, (hipStream_t)stream),
+                    "svdq_pack_lowrank_up");
+}
+
 static int quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
                         int K, int r, uint8_t* xq, uint16_t* x_scales, float* T, void* stream,
                         int codes, const char* name) {

@@ -80,31 +80,48 @@ hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16
   return hipGetLastError();
 }
 
-// Low-rank factor relayout (offline weight preparation, like the residual packing above): the
-// [K, r] factor L1 of the 16-bit branch (SVDQ "technical principles") becomes [r, K], each
-// rank's K values contiguous, the layout the activation pass reads (one row's 64-value group
-// slice of a rank per 16-byte pair).  A plain transpose through LDS in 64 x 64 tiles (bf16
-// values copied, no arithmetic).
-__global__ __launch_bounds__(256) void pack_lowrank_kernel(const uint16_t* __restrict__ L1, int K,
-                                                           int r, uint16_t* __restrict__ L1p) {
+// Low-rank factor relayouts (offline weight preparation, like the residual packing above), for
+// the two factors of the 16-bit branch (SVDQ "technical principles"): L1 [K, r] becomes
+// [r, K], each rank's K values contiguous, the layout the activation pass reads (one row's
+// 64-value group slice of a rank per 16-byte pair); L2 [r, N] becomes [N, r], each column's
+// ranks contiguous, the layout the GEMM epilogue reads (8 ranks of a column per 16-byte
+// fragment).  Plain transposes through LDS in 64 x 64 tiles (bf16 values copied, no
+// arithmetic).
+// bf16 transpose dst [cols, rows] = src [rows, cols]^T through a 64 x 65 LDS tile (both the
+// loads and the stores coalesced); block (x, y) covers columns 64 x and rows 64 y
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             int rows, int cols,
+                                                             uint16_t* __restrict__ dst) {
   __shared__ uint16_t tile[64][65];
-  const int k0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kk = i / 64, jj = i % 64;  // coalesced over the rank index of a row of L1
-    if (k0 + kk < K && j0 + jj < r) tile[kk][jj] = L1[(size_t)(k0 + kk) * r + j0 + jj];
+    const int rr = i / 64, cc = i % 64;  // coalesced along a row of src
+    if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = src[(size_t)(r0 + rr) * cols + c0 + cc];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int jj = i / 64, kk = i % 64;  // coalesced over k of a row of L1p
-    if (k0 + kk < K && j0 + jj < r) L1p[(size_t)(j0 + jj) * K + k0 + kk] = tile[kk][jj];
+    const int cc = i / 64, rr = i % 64;  // coalesced along a row of dst
+    if (r0 + rr < rows && c0 + cc < cols) dst[(size_t)(c0 + cc) * rows + r0 + rr] = tile[rr][cc];
   }
 }
 
+static hipError_t launch_transpose(const uint16_t* src, int rows, int cols, uint16_t* dst,
+                                   hipStream_t stream) {
+  const dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, src, rows, cols, dst);
+  return hipGetLastError();
+}
+
+// L1 [K, r] -> L1p [r, K]
 hipError_t launch_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p,
                                hipStream_t stream) {
-  const dim3 grid((K + 63) / 64, (r + 63) / 64);
-  hipLaunchKernelGGL(pack_lowrank_kernel, grid, dim3(256), 0, stream, L1, K, r, L1p);
-  return hipGetLastError();
+  return launch_transpose(L1, K, r, L1p, stream);
+}
+
+// L2 [r, N] -> L2p [N, r]
+hipError_t launch_pack_lowrank_up(const uint16_t* L2, int r, int N, uint16_t* L2p,
+                                  hipStream_t stream) {
+  return launch_transpose(L2, r, N, L2p, stream);
 }
 
 }  // namespace svdq

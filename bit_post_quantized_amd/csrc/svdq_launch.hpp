@@ -16,6 +16,10 @@ hipError_t launch_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16
 hipError_t launch_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p,
                                hipStream_t stream);
 
+// L2 [r, N] -> L2p [N, r] (the GEMM epilogue's layout of the up-projection factor)
+hipError_t launch_pack_lowrank_up(const uint16_t* L2, int r, int N, uint16_t* L2p,
+                                  hipStream_t stream);
+
 // code containers of the activation pass: INT4 as nibbles [M, K/2], INT4 as the tiled BF6
 // container, or the 8-bit codes of the W4A8 variant [M, K] (int8)
 constexpr int kCodesNibbles = 0, kCodesBf6 = 1, kCodesInt8 = 2;

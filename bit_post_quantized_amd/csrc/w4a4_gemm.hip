@@ -258,15 +258,10 @@ void w4a4_gemm_kernel(
       v8bf Bt[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        // L2 [r, N]: this lane's column, ranks kk .. kk + 7
-        uint32_t b[4] = {0u, 0u, 0u, 0u};
-        if (kv) {
-          const uint16_t* lp = L2 + (size_t)kk * No + min(col0 + 16 * j + rl, No - 1);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            b[q] = (uint32_t)lp[(size_t)(2 * q) * No] | ((uint32_t)lp[(size_t)(2 * q + 1) * No] << 16);
-        }
-        Bt[j] = __builtin_bit_cast(v8bf, v4u{b[0], b[1], b[2], b[3]});
+        // L2p [N, r]: this lane's column, ranks kk .. kk + 7
+        v4u b = v4u{0u, 0u, 0u, 0u};
+        if (kv) b = *reinterpret_cast<const v4u*>(L2 + (size_t)min(col0 + 16 * j + rl, No - 1) * r + kk);
+        Bt[j] = __builtin_bit_cast(v8bf, b);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {

@@ -49,7 +49,7 @@ constexpr int RT = TM / 32, CT = TN / 32;     // 32 x 32 tiles along M and N
 constexpr int kFrag = kE3m2Block;             // one 32-row block x one group, 64 lane slots
 constexpr int kOpA = RT * KS * kFrag;         // [tile][group][64 slots][24 B]
 constexpr int kOpB = CT * KS * kFrag;
-constexpr int kScA = KS * TM * 4;             // [group][row], one zero-extended fp16 per dword
+constexpr int kScA = KS * TM * 4;             // [row][group], one zero-extended fp16 per dword
 constexpr int kScB = KS * TN * 4;
 constexpr int kStage = kScA + kScB + kOpA + kOpB;  // s_x, s_w, A, B
 constexpr int kLds = NB * kStage;
@@ -76,9 +76,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // The four resources of one stage (first group g0), all uniform (scalar registers): the codes
 // of the workgroup's row and column blocks from group g0 to the end of the tensor (counted in
 // 32-bit units: blocks left = (row blocks from the tile on) * G - g0 <= 2^29 for M * K <= 2^40,
-// capped at 2^31 - 1 bytes, beyond every offset a stage uses), and the TM (TN) scales of the
-// wave's group g0 + s_gq from the tile's first row -- or nothing when that group does not exist
-// (the second group of an odd G's last stage).
+// capped at 2^31 - 1 bytes, beyond every offset a stage uses); the activation scales of the
+// tile's rows from group g0 on (both groups of the stage); and the TN weight scales of the
+// wave's group g0 + s_gq -- or nothing when that group does not exist (the second group of an
+// odd G's last stage).
 struct StageRsrc {
   __amdgpu_buffer_rsrc_t a, b, sx, sw;
 };
@@ -95,10 +96,11 @@ __device__ __forceinline__ StageRsrc stage_rsrc(const uint8_t* xq, const uint8_t
   if constexpr (!PARTIALS) {
     const int g = g0 + s_gq;
     const bool live = g < G;
-    // s_x is [M, G]: from the tile's first row at group g, this lane's row is G scales further
-    // per row (the lane offset); the range covers the tile's rows
-    R.sx = buffer_rsrc(x_scales + (size_t)m_tile * G + min(g, G - 1),
-                       live ? min(M - m_tile, TM) * G * 2 - 2 * min(g, G - 1) : 0);
+    // s_x is [M, G]: from the tile's first row at group g0; a lane's offset selects its row and
+    // one of the stage's two groups.  The range ends after the tile's last row, so the missing
+    // second group of an odd G's last stage reads nothing there (elsewhere it reads the next
+    // row's first scale, which is never used)
+    R.sx = buffer_rsrc(x_scales + (size_t)m_tile * G + g0, min(M - m_tile, TM) * G * 2 - 2 * g0);
     R.sw = buffer_rsrc(w_scales + (size_t)min(g, G - 1) * N + n_tile, live ? 2 * TN : 0);
   } else {
     R.sx = R.a;
@@ -152,11 +154,14 @@ void w4a4_gemm_e3m2_kernel(
     a_off[j] = (uint32_t)((size_t)(min(mt + tile, mblk - 1) - mt) * G * kFrag + within);
     b_off[j] = (uint32_t)((size_t)(min(nt + tile, nblk - 1) - nt) * G * kFrag + within);
   }
-  // scales: thread t loads s_x of (group t / TM, row t % TM) and s_w of (group t / TN,
-  // column t % TN) as 2-byte direct loads, which land zero-extended in dword t of the area;
-  // the group of a scale load is uniform over the wave
+  // scales: thread t loads s_x of (row t / 2, group t % 2 of the stage) -- the two groups of a
+  // row are adjacent in [M, G], so a wave reads 32 contiguous pairs instead of 64 scattered
+  // halves (measured 2-3 % of the kernel) -- and s_w of (group t / TN, column t % TN), as
+  // 2-byte direct loads, which land zero-extended in dword t of the area ([row][group] for
+  // s_x, [group][column] for s_w); the group of an s_w load is uniform over the wave
   const int s_gq = wave >> 1;
-  const uint32_t sx_lane = 2u * (uint32_t)G * (uint32_t)(min(m_tile + tid % TM, M - 1) - m_tile);
+  const uint32_t sx_lane =
+      2u * ((uint32_t)G * (uint32_t)(min(m_tile + (tid >> 1), M - 1) - m_tile) + (uint32_t)(tid & 1));
   const uint32_t sw_lane = 2u * (uint32_t)(min(n_tile + tid % TN, N - 1) - n_tile);
 
   auto issue_stage = [&](int s) {
@@ -217,7 +222,7 @@ void w4a4_gemm_e3m2_kernel(
   // to element e ^ 1 of the partial, so the dequantization FMA acc[e] += p[e] * s[e ^ 1] reads
   // its three operands from different VGPR banks (acc, p and s are 16-register tiles whose
   // element e would otherwise share bank e % 4, which stalls the FMA).
-  const int sa_off = (32 * 2 * wm + ((lane & 31) ^ 1)) * 4;      // + (gg * TM + 32 i) * 4
+  const int sa_off = 2 * (32 * 2 * wm + ((lane & 31) ^ 1)) * 4;  // + (64 i + gg) * 4
   const int sb_off = kScA + (32 * 2 * wn + (lane & 31)) * 4;    // + (gg * TN + 32 j) * 4
   const uint32_t sb_keep = lane < 32 ? 0xFFFFFFFFu : 0u;
 
@@ -236,16 +241,12 @@ void w4a4_gemm_e3m2_kernel(
 
   // ---- epilogue operands staged in LDS while the last stages run.  From iteration
   //      max(S - 2, 0) on, buffer S % NB holds no stage any more; T [128 rows x r] fp32,
-  //      L2 [r x 128 cols] bf16 and the bias of the tile are copied into it with the same
-  //      direct-to-LDS loads: T chunk-column-major (16-byte chunk c of row x at chunk index
-  //      c * 128 + x), L2 as its rows' 16-byte chunks of 8 columns ([rank][128 columns]), so
-  //      that the epilogue's reads are conflict-free.  L2's chunks are 16-byte aligned only when
-  //      N % 8 == 0; otherwise the epilogue reads L2 from global memory and the chunk loads
-  //      read nothing (an empty range, the same load count for every wave).  (Without a bias
+  //      L2p [128 cols x r] bf16 and the bias of the tile are copied into it with the same
+  //      direct-to-LDS loads, chunk-column-major (16-byte chunk c of row x at chunk index
+  //      c * 128 + x) so that the epilogue's fragment reads are conflict-free.  (Without a bias
   //      the bias slot loads the weight scales instead, so every wave issues the same count.)
   constexpr bool PRE = !PARTIALS && NTR > 0 && NTR * (TM * 16 * 4 + TN * 16 * 2) + TN * 4 <= kStage;
   constexpr int kPreT = 2 * NTR, kPreL = NTR, kPre = kPreT + kPreL + 1;  // loads per thread
-  const bool pre_l2 = N % 8 == 0;
   constexpr int kPreL2Off = NTR * TM * 16 * 4, kPreBiasOff = kPreL2Off + NTR * TN * 16 * 2;
   auto issue_prefetch = [&]() {
     if constexpr (PRE) {
@@ -255,14 +256,10 @@ void w4a4_gemm_e3m2_kernel(
         const int p = j * THREADS + tid, c = p / TM, x = p % TM;
         __builtin_amdgcn_global_load_lds(T + (size_t)min(m_tile + x, M - 1) * r + 4 * c, SVDQ_LDS(pb + j * 4096 + wave * 1024), 16, 0, 0);
       }
-      // L2 chunk p = 256 j + t: rank p / 16, columns n_tile + 8 (p % 16) .. + 7 (a chunk past
-      // N reads the next rank's first columns or nothing: those columns are not stored)
-      const __amdgpu_buffer_rsrc_t rl =
-          buffer_rsrc(L2 + n_tile, pre_l2 ? (int)min((long long)((r - 1) * N + N - n_tile) * 2, 0x7FFFFFFFLL) : 0);
 #pragma unroll
       for (int j = 0; j < kPreL; ++j) {
-        const int p = j * THREADS + tid, k = p / 16, c = p % 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, SVDQ_LDS(pb + kPreL2Off + j * 4096 + wave * 1024), 16, (uint32_t)(k * N + 8 * c) * 2u, 0, 0, 0);
+        const int p = j * THREADS + tid, c = p / TN, x = p % TN;
+        __builtin_amdgcn_global_load_lds(L2 + (size_t)min(n_tile + x, N - 1) * r + 8 * c, SVDQ_LDS(pb + kPreL2Off + j * 4096 + wave * 1024), 16, 0, 0);
       }
       const int bc = min(n_tile + (wave & 1) * 64 + lane, N - 1);
       __builtin_amdgcn_global_load_lds(bias ? bias + bc : w_scales + bc, SVDQ_LDS(pb + kPreBiasOff + (wave & 1) * 256), 2, 0, 0);
@@ -284,7 +281,7 @@ void w4a4_gemm_e3m2_kernel(
       F.A[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
       F.B[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, 0, 0};
       if constexpr (!PARTIALS) {
-        const uint32_t sx = *reinterpret_cast<const uint32_t*>(st + sa_off + (gg * TM + 32 * i) * 4);
+        const uint32_t sx = *reinterpret_cast<const uint32_t*>(st + sa_off + (64 * i + gg) * 4);
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + sb_off + (gg * TN + 32 * i) * 4);
         F.SA[i] = __builtin_bit_cast(v4h, v2u{sx & sb_keep, 0u});
         F.SB[i] = __builtin_bit_cast(v4h, v2u{sw & sb_keep, 0u});
@@ -428,26 +425,8 @@ void w4a4_gemm_e3m2_kernel(
       const int k8 = kk + 8 * hi;  // this lane's 8 rank indices: T chunks k8 / 4 and + 1
       v8bf Bt[2], At[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // L2 [r, N]: this lane's column, ranks k8 .. k8 + 7 (from LDS, or from global memory
-        // when N % 8 != 0)
-        uint32_t b[4];
-        const int cl = wn * 64 + 32 * j + l32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t lo, hi2;
-          if (pre_l2) {
-            lo = *reinterpret_cast<const uint16_t*>(pb + kPreL2Off + ((k8 + 2 * q) * TN + cl) * 2);
-            hi2 = *reinterpret_cast<const uint16_t*>(pb + kPreL2Off + ((k8 + 2 * q + 1) * TN + cl) * 2);
-          } else {
-            const int c = min(col0 + 32 * j + l32, No - 1);
-            lo = L2[(size_t)(k8 + 2 * q) * No + c];
-            hi2 = L2[(size_t)(k8 + 2 * q + 1) * No + c];
-          }
-          b[q] = lo | (hi2 << 16);
-        }
-        Bt[j] = __builtin_bit_cast(v8bf, v4u{b[0], b[1], b[2], b[3]});
-      }
+      for (int j = 0; j < 2; ++j)  // L2p: this lane's column, ranks k8 .. k8 + 7
+        Bt[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(pb + kPreL2Off + ((k8 / 8) * TN + wn * 64 + 32 * j + l32) * 16));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int x = wm * 64 + 32 * i + l32;
@@ -468,15 +447,8 @@ void w4a4_gemm_e3m2_kernel(
       const int k8 = kk + 8 * hi;  // this lane's 8 rank indices
       v8bf Bt[2], At[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // L2 [r, N]: this lane's column, ranks k8 .. k8 + 7
-        const uint16_t* lp = L2 + (size_t)k8 * No + min(col0 + 32 * j + l32, No - 1);
-        uint32_t b[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          b[q] = (uint32_t)lp[(size_t)(2 * q) * No] | ((uint32_t)lp[(size_t)(2 * q + 1) * No] << 16);
-        Bt[j] = __builtin_bit_cast(v8bf, v4u{b[0], b[1], b[2], b[3]});
-      }
+      for (int j = 0; j < 2; ++j)  // L2p: this lane's column, ranks k8 .. k8 + 7
+        Bt[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(L2 + (size_t)min(col0 + 32 * j + l32, No - 1) * r + k8));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const v4f* tp = reinterpret_cast<const v4f*>(T + (size_t)min(row0 + 32 * i + l32, Mo - 1) * r + k8);

@@ -8,8 +8,9 @@ it is the offline preparation a toolbox performs once per checkpoint, not part o
 per-token path.
 
 Forward (device): ``svdq_quantize_act`` then ``svdq_w4a4_gemm``, two launches on one stream.
-The factor L1 [K, r] is relaid out once to the activation pass's [r, K] by
-``svdq_pack_lowrank``; L2 [r, N] is read by the GEMM as it is.
+The factors are relaid out once, like the residual: L1 [K, r] to the activation pass's
+[r, K] by ``svdq_pack_lowrank``, L2 [r, N] to the GEMM epilogue's [N, r] by
+``svdq_pack_lowrank_up``.
 With ``e3m2=True`` the codes travel as BF6 (E3M2) values and the ``*_e3m2`` entry points run
 the GEMM on the FP6 matrix units (same codes, scales and result; the faster path on gfx950).
 """
@@ -31,7 +32,7 @@ class PackedWeights:
     rank: int
     inv_lambda: torch.Tensor  # fp32 [K]
     L1p: torch.Tensor         # bf16 [r, K]  (the [K, r] factor, from svdq_pack_lowrank)
-    L2: torch.Tensor          # bf16 [r, N]
+    L2p: torch.Tensor         # bf16 [N, r]  (the [r, N] factor, from svdq_pack_lowrank_up)
     wq: torch.Tensor          # uint8 [N, K/2] (nibbles) or the tiled BF6 container of N rows
     w_scales: torch.Tensor    # fp16 [K/64, N]
     bias: Optional[torch.Tensor] = None  # bf16 [N]
@@ -96,7 +97,7 @@ def pack_device(hw: HostWeights, bias: Optional[torch.Tensor] = None, device="cu
                 e3m2: bool = False, keep_residual: bool = False) -> PackedWeights:
     """The device half of the weight conversion: the residual's INT4 codes and scales
     (``svdq_pack_weights``, or ``svdq_pack_weights_e3m2`` for the BF6 container) and the factor
-    relayout (``svdq_pack_lowrank``)."""
+    relayouts (``svdq_pack_lowrank``, ``svdq_pack_lowrank_up``)."""
     K, N = hw.R32.shape
     rank = hw.L1b.shape[1]
     R32 = hw.R32.to(device).contiguous()
@@ -109,7 +110,7 @@ def pack_device(hw: HostWeights, bias: Optional[torch.Tensor] = None, device="cu
         binding.svdq_pack_weights(R32, wq, w_scales)
     return PackedWeights(
         K=K, N=N, rank=rank, inv_lambda=hw.inv_lambda.to(device),
-        L1p=pack_lowrank(hw.L1b.to(device)), L2=hw.L2b.contiguous().to(device),
+        L1p=pack_lowrank(hw.L1b.to(device)), L2p=pack_lowrank_up(hw.L2b.to(device)),
         wq=wq, w_scales=w_scales,
         bias=None if bias is None else bias.to(device, torch.bfloat16).contiguous(), e3m2=e3m2,
         R32=R32 if keep_residual else None, lam=hw.lam)
@@ -130,6 +131,15 @@ def pack_lowrank(L1: torch.Tensor) -> torch.Tensor:
     if r:
         binding.svdq_pack_lowrank(L1.contiguous(), L1p)
     return L1p
+
+
+def pack_lowrank_up(L2: torch.Tensor) -> torch.Tensor:
+    """L2 bf16 [r, N] on the device -> L2p [N, r] (``svdq_pack_lowrank_up``); [N, 0] for r = 0."""
+    r, N = L2.shape
+    L2p = torch.empty(N, r, dtype=torch.bfloat16, device=L2.device)
+    if r:
+        binding.svdq_pack_lowrank_up(L2.contiguous(), L2p)
+    return L2p
 
 
 def attach_lora(pw: PackedWeights, A: torch.Tensor, B: torch.Tensor,
@@ -154,8 +164,8 @@ def attach_lora(pw: PackedWeights, A: torch.Tensor, B: torch.Tensor,
     A_hat = _bf16_rn(pw.lam.to("cpu", torch.float64)[:, None] * A.to("cpu", torch.float64))
     B_s = _bf16_rn(scale * B.to("cpu", torch.float64))
     L1p = torch.cat([pw.L1p, pack_lowrank(A_hat.to(dev))], dim=0).contiguous()
-    L2 = torch.cat([pw.L2, B_s.to(dev)], dim=0).contiguous()
-    return dataclasses.replace(pw, rank=r2, L1p=L1p, L2=L2)
+    L2p = torch.cat([pw.L2p, pack_lowrank_up(B_s.to(dev))], dim=1).contiguous()
+    return dataclasses.replace(pw, rank=r2, L1p=L1p, L2p=L2p)
 
 
 @dataclass
@@ -186,6 +196,6 @@ def forward(X: torch.Tensor, pw: PackedWeights, out: Optional[torch.Tensor] = No
     gemm = binding.svdq_w4a4_gemm_e3m2 if pw.e3m2 else binding.svdq_w4a4_gemm
     quantize(X, pw.inv_lambda, pw.L1p if pw.rank else None, pw.rank, act.xq, act.x_scales,
              act.T, stream)
-    gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales, pw.L2 if pw.rank else None,
+    gemm(act.xq, act.x_scales, act.T, pw.wq, pw.w_scales, pw.L2p if pw.rank else None,
          pw.bias, pw.rank, out, stream)
     return out

@@ -16,7 +16,8 @@
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller; the library never allocates,
- *     frees or keeps them, holds no global state and is safe to call from several threads.
+ *     frees or keeps them, holds no global state (apart from the device scratch of
+ *     kv_int8_quant_pair_noalloc) and is safe to call from several threads.
  *   - Arrays are dense and row-major in the layout written next to each argument; fp16 and
  *     bf16 values are passed as their uint16 bit patterns.
  *   - Pointers marked "16B" must be 16-byte aligned.
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 7
+#define SVDQ_ABI_VERSION 8
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -83,6 +84,16 @@ int svdq_pack_weights(const float* R, int K, int N, uint8_t* wq, uint16_t* w_sca
 int svdq_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p, void* stream);
 
 /*
+ * svdq_pack_lowrank_up — relayout of the 16-bit branch's up-projection factor for the GEMM
+ * epilogue (offline weight preparation, like svdq_pack_lowrank).  Values are copied, not
+ * rounded.
+ *   L2    bf16 [r, N] (row-major: element (j, n) at L2[j * N + n])
+ *   L2p   bf16 [N, r] (element (j, n) at L2p[n * r + j]: each column's r values contiguous)
+ *   16 <= r <= 128, r % 16 == 0, 1 <= N <= 2^24.
+ */
+int svdq_pack_lowrank_up(const uint16_t* L2, int r, int N, uint16_t* L2p, void* stream);
+
+/*
  * svdq_quantize_act — one HBM pass over the activations: smoothing divide (a multiply by the
  * stored reciprocal inv_lambda), dynamic symmetric INT4 quantization per (token, 64-group)
  * (FLUX4 3.1 "dynamic activation quantization"; W4A8 3.1), and the low-rank down-projection
@@ -107,8 +118,8 @@ int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t
  *     P[g, m, n] = sum_{k in group g} qx[m, k] qw[n, k]   (exact int32).
  *   xq, x_scales, T   as written by svdq_quantize_act (T: 16B; may be NULL when r == 0)
  *   wq, w_scales      as written by svdq_pack_weights
- *   L2          bf16 [r, N] (row-major: element (j, n) at L2[j * N + n]) (16B); may be NULL
- *               when r == 0
+ *   L2p         bf16 [N, r], the factor L2 [r, N] as written by svdq_pack_lowrank_up (16B);
+ *               may be NULL when r == 0
  *   bias        bf16 [N] or NULL
  *   Y           [M, N], bf16 (out_dtype = SVDQ_OUT_BF16, round to nearest even) or fp32
  *               (SVDQ_OUT_FP32)                           16B
@@ -116,7 +127,7 @@ int svdq_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t
  *   0 <= r <= 128, r % 16 == 0.  The same limits hold for every GEMM entry point below.
  */
 int svdq_w4a4_gemm(const uint8_t* xq, const uint16_t* x_scales, const float* T,
-                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2p,
                    const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
                    void* stream);
 
@@ -159,7 +170,7 @@ int svdq_quantize_act_e3m2(const uint16_t* X, const float* inv_lambda, const uin
                            int M, int K, int r, uint8_t* xq6, uint16_t* x_scales, float* T,
                            void* stream);
 int svdq_w4a4_gemm_e3m2(const uint8_t* xq6, const uint16_t* x_scales, const float* T,
-                        const uint8_t* wq6, const uint16_t* w_scales, const uint16_t* L2,
+                        const uint8_t* wq6, const uint16_t* w_scales, const uint16_t* L2p,
                         const uint16_t* bias, int M, int N, int K, int r, void* Y,
                         int out_dtype, void* stream);
 int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N, int K,
@@ -184,7 +195,7 @@ int svdq_w4a4_partials_e3m2(const uint8_t* xq6, const uint8_t* wq6, int M, int N
 int svdq_quantize_act_a8(const uint16_t* X, const float* inv_lambda, const uint16_t* L1, int M,
                          int K, int r, int8_t* xq8, uint16_t* x_scales, float* T, void* stream);
 int svdq_w4a8_gemm(const int8_t* xq8, const uint16_t* x_scales, const float* T,
-                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2,
+                   const uint8_t* wq, const uint16_t* w_scales, const uint16_t* L2p,
                    const uint16_t* bias, int M, int N, int K, int r, void* Y, int out_dtype,
                    void* stream);
 int svdq_w4a8_partials(const int8_t* xq8, const uint8_t* wq, int M, int N, int K, int32_t* P,

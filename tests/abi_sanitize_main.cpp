@@ -46,6 +46,8 @@ int main() {
   EXPECT(svdq_pack_lowrank(u16(F), INT_MAX / 64 * 64, 16, u16(F), nullptr) == SVDQ_ESHAPE);
   EXPECT(svdq_pack_lowrank(u16(F), 128, INT_MAX, u16(F), nullptr) == SVDQ_ESHAPE);
   EXPECT(svdq_pack_lowrank(u16(F), 128, INT_MIN, u16(F), nullptr) == SVDQ_EINVAL);
+  EXPECT(svdq_pack_lowrank_up(u16(F), 16, INT_MAX, u16(F), nullptr) == SVDQ_ESHAPE);
+  EXPECT(svdq_pack_lowrank_up(u16(F), INT_MIN, 64, u16(F), nullptr) == SVDQ_EINVAL);
 
   // ---- activation pass (three containers)
   EXPECT(svdq_quantize_act(u16(F), f32(F), u16(F), INT_MAX, INT_MAX / 64 * 64, 16, u8(F), u16(F),

@@ -79,13 +79,19 @@ def oracle_act(case):
     return osq.quantize_act(d["X"], pw["inv_lambda"], pw["L1b"])
 
 
+def pack_l2(L2):
+    """L2 [r, N] on the device -> L2p [N, r] through the library's relayout."""
+    from bit_post_quantized_amd import layer
+    return layer.pack_lowrank_up(L2)
+
+
 def device_weights(case):
     """Oracle-prepared weights in the C-ABI layouts on the device."""
     d, pw, packed, r = case
     return dict(
         inv_lambda=dev(pw["inv_lambda"]),
         L1p=dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None,  # [r, K]
-        L2=dev_bf16(bf16_to_bits(pw["L2b"])) if r else None,      # [r, N]
+        L2p=pack_l2(dev_bf16(bf16_to_bits(pw["L2b"]))) if r else None,  # [N, r]
         R32=dev(pw["R32"]),
         bias=dev_bf16(d["bias"]) if d["bias"] is not None else None,
     )

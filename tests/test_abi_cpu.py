@@ -26,14 +26,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.svdq_abi_version() == 7
+    assert lib.svdq_abi_version() == 8
     assert lib.svdq_status_str(0) == b"ok"
     assert lib.svdq_status_str(2) == b"unsupported shape"
     assert lib.svdq_status_str(99) == b"unknown status"
@@ -62,6 +62,17 @@ def test_pack_lowrank_validation(lib):
     assert f(FAKE, 128, 0, FAKE, None) == binding.SVDQ_ESHAPE    # nothing to relay out
     assert f(None, 128, 16, FAKE, None) == binding.SVDQ_EINVAL
     assert f(FAKE, 128, 16, None, None) == binding.SVDQ_EINVAL
+
+
+def test_pack_lowrank_up_validation(lib):
+    f = lib.svdq_pack_lowrank_up
+    assert f(FAKE, 24, 128, FAKE, None) == binding.SVDQ_ESHAPE       # r % 16
+    assert f(FAKE, 144, 128, FAKE, None) == binding.SVDQ_ESHAPE      # r > 128
+    assert f(FAKE, 0, 128, FAKE, None) == binding.SVDQ_ESHAPE        # nothing to relay out
+    assert f(FAKE, 16, 0, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, 16, (1 << 24) + 1, FAKE, None) == binding.SVDQ_ESHAPE
+    assert f(None, 16, 128, FAKE, None) == binding.SVDQ_EINVAL
+    assert f(FAKE, 16, 128, None, None) == binding.SVDQ_EINVAL
 
 
 def test_quantize_act_validation(lib):

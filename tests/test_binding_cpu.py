@@ -52,7 +52,7 @@ def _cases():
     act = dict(X=([M, K], bf16), inv_lambda=([K], f32), L1p=([R, K], bf16),
                x_scales=([M, G], f16), T=([M, R], f32))
     gemm = dict(x_scales=([M, G], f16), T=([M, R], f32), w_scales=([G, N], f16),
-                L2=([R, N], bf16), bias=([N], bf16), Y=([M, N], bf16))
+                L2p=([N, R], bf16), bias=([N], bf16), Y=([M, N], bf16))
     kv_t, heads, dim = 70, 2, 64
     C = heads * dim
     return [
@@ -61,18 +61,19 @@ def _cases():
         (B.svdq_pack_weights_e3m2, ["R", "wq6", "w_scales"],
          dict(R=([K, N], f32), wq6=([e3(N)], u8), w_scales=([G, N], f16)), {}),
         (B.svdq_pack_lowrank, ["L1", "L1p"], dict(L1=([K, R], bf16), L1p=([R, K], bf16)), {}),
+        (B.svdq_pack_lowrank_up, ["L2", "L2p"], dict(L2=([R, N], bf16), L2p=([N, R], bf16)), {}),
         (B.svdq_quantize_act, ["X", "inv_lambda", "L1p", "r", "xq", "x_scales", "T"],
          dict(act, xq=([M, K // 2], u8)), dict(r=R)),
         (B.svdq_quantize_act_e3m2, ["X", "inv_lambda", "L1p", "r", "xq6", "x_scales", "T"],
          dict(act, xq6=([e3(M)], u8)), dict(r=R)),
         (B.svdq_quantize_act_a8, ["X", "inv_lambda", "L1p", "r", "xq8", "x_scales", "T"],
          dict(act, xq8=([M, K], i8)), dict(r=R)),
-        (B.svdq_w4a4_gemm, ["xq", "x_scales", "T", "wq", "w_scales", "L2", "bias", "r", "Y"],
+        (B.svdq_w4a4_gemm, ["xq", "x_scales", "T", "wq", "w_scales", "L2p", "bias", "r", "Y"],
          dict(gemm, xq=([M, K // 2], u8), wq=([N, K // 2], u8)), dict(r=R)),
         (B.svdq_w4a4_gemm_e3m2,
-         ["xq6", "x_scales", "T", "wq6", "w_scales", "L2", "bias", "r", "Y"],
+         ["xq6", "x_scales", "T", "wq6", "w_scales", "L2p", "bias", "r", "Y"],
          dict(gemm, xq6=([e3(M)], u8), wq6=([e3(N)], u8)), dict(r=R)),
-        (B.svdq_w4a8_gemm, ["xq8", "x_scales", "T", "wq", "w_scales", "L2", "bias", "r", "Y"],
+        (B.svdq_w4a8_gemm, ["xq8", "x_scales", "T", "wq", "w_scales", "L2p", "bias", "r", "Y"],
          dict(gemm, xq8=([M, K], i8), wq=([N, K // 2], u8)), dict(r=R)),
         (B.svdq_w4a4_partials, ["xq", "wq", "P"],
          dict(xq=([M, K // 2], u8), wq=([N, K // 2], u8), P=([G, M, N], i32)), {}),
@@ -148,8 +149,9 @@ def _case(fn):
 @pytest.mark.parametrize("fn,name,bad", [
     (B.svdq_w4a4_gemm, "x_scales", [G, M]),       # group-major instead of [M, K/64]
     (B.svdq_w4a4_gemm_e3m2, "x_scales", [G, M]),
-    (B.svdq_w4a4_gemm, "L2", [N, R]),             # transposed factor instead of [r, N]
-    (B.svdq_w4a4_gemm_e3m2, "L2", [N, R]),
+    (B.svdq_w4a4_gemm, "L2p", [R, N]),            # the unpacked factor instead of [N, r]
+    (B.svdq_w4a4_gemm_e3m2, "L2p", [R, N]),
+    (B.svdq_pack_lowrank_up, "L2p", [R, N]),
     (B.svdq_w4a8_gemm, "T", [R, M]),
     (B.svdq_quantize_act, "x_scales", [G, M]),
     (B.svdq_quantize_act, "L1p", [K, R]),          # the unpacked factor

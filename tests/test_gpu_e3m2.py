@@ -92,7 +92,7 @@ def test_gemm_e3m2_output_within_tolerance(gpu_lib, name, bias):
     wq, ws = _gpu_pack6(case)
     xq, xs, T = _gpu_act6(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm_e3m2(xq, xs, T, wq, ws, w["L2p"], w["bias"], r, Y)
     torch.cuda.synchronize()
     Y_ref = oracle_output(cid, M_, K_, N_, d["bias"])
     err = max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref)
@@ -109,7 +109,7 @@ def test_gemm_e3m2_short_k(gpu_lib, cid, K):
     wq6, ws = _gpu_pack6(case)
     xq6, xs, T = _gpu_act6(case)
     Y = torch.empty(70, 100, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2p"], w["bias"], r, Y)
     torch.cuda.synchronize()
     ref = oracle_act(case)
     Y_ref = osq.linear_output(ref["codes"], ref["s_x"], packed["codes"], packed["s_w"],
@@ -175,8 +175,8 @@ def test_e3m2_and_nibble_routes_agree(gpu_lib):
     wq6, ws6 = _gpu_pack6(case)
     Y4 = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Y6 = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y4)
-    B.svdq_w4a4_gemm_e3m2(xq6, xs6, T6, wq6, ws6, w["L2"], w["bias"], r, Y6)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2p"], w["bias"], r, Y4)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs6, T6, wq6, ws6, w["L2p"], w["bias"], r, Y6)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(osq.unpack_e3m2_tiled(xq6.cpu().numpy(), M, K), osq.unpack_nibbles(xq.cpu().numpy()))
     np.testing.assert_array_equal(osq.unpack_e3m2_tiled(wq6.cpu().numpy(), N, K), osq.unpack_nibbles(wq.cpu().numpy()))
@@ -254,7 +254,7 @@ def test_e3m2_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     xs = torch.full((G * M + 8,), -3.0, dtype=torch.float16, device="cuda")
     T = torch.full((M + 1, max(r, 1)), -7.0, dtype=torch.float32, device="cuda")
     L1t = dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None
-    L2t = dev_bf16(bf16_to_bits(pw["L2b"])) if r else None  # [r, N]
+    L2t = dev_bf16(np.ascontiguousarray(bf16_to_bits(pw["L2b"]).T)) if r else None  # [N, r]
     Tv = T[:M] if r else None
     B.svdq_quantize_act_e3m2(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq6[:BX],
                              xs[:G * M].view(M, G), Tv)
@@ -283,8 +283,8 @@ def test_e3m2_fp32_output_and_determinism(gpu_lib):
     xq6, xs, T = _gpu_act6(case)
     Ya = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Yb = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Ya)
-    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2"], w["bias"], r, Yb)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2p"], w["bias"], r, Ya)
+    B.svdq_w4a4_gemm_e3m2(xq6, xs, T, wq6, ws, w["L2p"], w["bias"], r, Yb)
     torch.cuda.synchronize()
     assert torch.equal(Ya, Yb)
     ref = oracle_act(case)

@@ -1,5 +1,5 @@
-"""The product path through layer.py on the GPU: the factor relayout (svdq_pack_lowrank)
-bit-exact, and layer.pack_device + layer.forward -- the calls bench.py times -- at the full
+"""The product path through layer.py on the GPU: the factor relayouts (svdq_pack_lowrank,
+svdq_pack_lowrank_up) bit-exact, and layer.pack_device + layer.forward -- the calls bench.py times -- at the full
 FFN up-projection shape, every output row against the oracle's fp64 output.
 
 The host half of the weight preparation (layer.prepare_host) is pinned against the oracle on
@@ -25,6 +25,16 @@ def test_pack_lowrank_bitexact(gpu_lib, K, r):
     L1p = layer.pack_lowrank(dev_bf16(bits))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host_u16(L1p), np.ascontiguousarray(bits.T))
+
+
+@pytest.mark.parametrize("r,N", [(16, 64), (16, 1), (32, 12288), (32, 3072), (48, 200),
+                                 (128, 130)])
+def test_pack_lowrank_up_bitexact(gpu_lib, r, N):
+    rng = np.random.default_rng(r * 7 + N)
+    bits = rng.integers(0, 1 << 16, (r, N), dtype=np.uint32).astype(np.uint16)
+    L2p = layer.pack_lowrank_up(dev_bf16(bits))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_u16(L2p), np.ascontiguousarray(bits.T))
 
 
 def _host_weights(pw):

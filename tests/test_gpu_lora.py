@@ -9,7 +9,7 @@ import torch
 from bit_post_quantized_amd import binding as B
 from oracle import svdquant as osq
 from oracle.numerics import bf16_to_bits
-from tests.gpu_cases import dev, dev_bf16, host_u16, linear_case, max_abs_rel
+from tests.gpu_cases import dev, dev_bf16, host_u16, linear_case, max_abs_rel, pack_l2
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -32,7 +32,7 @@ def test_lora_branch_parity(gpu_lib, rl, e3m2):
                               L2p, d["bias"])
 
     L1t = dev_bf16(bf16_to_bits(L1p.T))
-    L2t = dev_bf16(bf16_to_bits(L2p))  # [r, N]
+    L2t = pack_l2(dev_bf16(bf16_to_bits(L2p)))  # [r, N] -> [N, r]
     inv = dev(pw["inv_lambda"])
     R32 = dev(pw["R32"])
     bias = dev_bf16(d["bias"])

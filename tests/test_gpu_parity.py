@@ -109,7 +109,7 @@ def test_gemm_output_within_tolerance(gpu_lib, name, bias):
     wq, ws = _gpu_pack(case)
     xq, xs, T = _gpu_act(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2p"], w["bias"], r, Y)
     torch.cuda.synchronize()
     Y_ref = oracle_output(cid, M_, K_, N_, d["bias"])
     err = max_abs_rel(Y.float().cpu().numpy().astype(np.float64), Y_ref)
@@ -210,7 +210,7 @@ def test_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     xs = torch.full((G * M + 8,), -3.0, dtype=torch.float16, device="cuda")
     T = torch.full((M + 1, max(r, 1)), -7.0, dtype=torch.float32, device="cuda")
     L1t = dev_bf16(bf16_to_bits(pw["L1b"].T)) if r else None
-    L2t = dev_bf16(bf16_to_bits(pw["L2b"])) if r else None  # [r, N]
+    L2t = dev_bf16(np.ascontiguousarray(bf16_to_bits(pw["L2b"]).T)) if r else None  # [N, r]
     Tv = T[:M] if r else None
     B.svdq_quantize_act(dev_bf16(d["X"]), dev(pw["inv_lambda"]), L1t, r, xq[:M],
                         xs[:G * M].view(M, G), Tv)
@@ -240,9 +240,9 @@ def test_fp32_output_and_determinism(gpu_lib):
     xq, xs, T = _gpu_act(case)
     Ya = torch.empty(M, N, dtype=torch.float32, device="cuda")
     Yb = torch.empty(M, N, dtype=torch.float32, device="cuda")
-    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2"], w["bias"], r, Ya)
+    B.svdq_w4a4_gemm(xq, xs, T, wq, ws, w["L2p"], w["bias"], r, Ya)
     xq2, xs2, T2 = _gpu_act(case)
-    B.svdq_w4a4_gemm(xq2, xs2, T2, wq, ws, w["L2"], w["bias"], r, Yb)
+    B.svdq_w4a4_gemm(xq2, xs2, T2, wq, ws, w["L2p"], w["bias"], r, Yb)
     torch.cuda.synchronize()
     assert torch.equal(Ya, Yb) and torch.equal(T, T2)
     ref = oracle_act(case)

@@ -55,7 +55,7 @@ def test_w4a8_gemm_output_within_tolerance(gpu_lib, name, bias):
     N = pw["R32"].shape[1]
     w, wq, ws, xq8, xs, T = _gpu(case)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    B.svdq_w4a8_gemm(xq8, xs, T, wq, ws, w["L2"], w["bias"], r, Y)
+    B.svdq_w4a8_gemm(xq8, xs, T, wq, ws, w["L2p"], w["bias"], r, Y)
     torch.cuda.synchronize()
     ref = osq.quantize_act_a8(d["X"], pw["inv_lambda"], pw["L1b"])
     if name in FULL:

@@ -19,19 +19,20 @@ def _packed(pw, r):
     return layer.PackedWeights(
         K=K, N=N, rank=r, inv_lambda=torch.from_numpy(pw["inv_lambda"]),
         L1p=torch.from_numpy(bf16_to_bits(pw["L1b"].T).view(np.int16)).view(torch.bfloat16),
-        L2=torch.from_numpy(bf16_to_bits(pw["L2b"]).view(np.int16)).view(torch.bfloat16),
+        L2p=torch.from_numpy(bf16_to_bits(pw["L2b"].T).view(np.int16)).view(torch.bfloat16),
         wq=torch.zeros(1, dtype=torch.uint8), w_scales=torch.zeros(1, dtype=torch.float16),
         lam=torch.from_numpy(pw["lam32"]))
 
 
-def _host_pack_lowrank(L1, L1p):
-    """Host stand-in for the device relayout (the library needs a GPU): L1 [K, r] -> [r, K]."""
-    L1p.copy_(L1.t())
+def _host_transpose(src, dst):
+    """Host stand-in for the device relayouts (the library needs a GPU): dst = src^T."""
+    dst.copy_(src.t())
 
 
 @pytest.mark.parametrize("rl,scale", [(16, 1.0), (32, 0.375)])
 def test_attach_lora_matches_the_oracle_bit_for_bit(rl, scale, monkeypatch):
-    monkeypatch.setattr(binding, "svdq_pack_lowrank", _host_pack_lowrank)
+    monkeypatch.setattr(binding, "svdq_pack_lowrank", _host_transpose)
+    monkeypatch.setattr(binding, "svdq_pack_lowrank_up", _host_transpose)
     d = make_linear(2, M=40, K=256, N=80, seed=3)
     pw = osq.prepare_weights(d["X"], d["W"], 0.5, 16)
     rng = np.random.default_rng(9)
@@ -42,7 +43,7 @@ def test_attach_lora_matches_the_oracle_bit_for_bit(rl, scale, monkeypatch):
     out = layer.attach_lora(base, torch.from_numpy(A), torch.from_numpy(B), scale)
     assert out.rank == 16 + rl
     np.testing.assert_array_equal(_bits(out.L1p), bf16_to_bits(L1p.T))
-    np.testing.assert_array_equal(_bits(out.L2), bf16_to_bits(L2p))
+    np.testing.assert_array_equal(_bits(out.L2p), bf16_to_bits(L2p.T))
     assert out.wq is base.wq and out.w_scales is base.w_scales  # no re-quantization
 
 
