@@ -271,26 +271,45 @@ void w4a4_gemm_e3m2_kernel(
     v8i A[2], B[2];
     v4h SA[2], SB[2];
   };
+  // Per-lane LDS offsets of stage s's operands, one add each per stage from an opaque stage
+  // offset.  (Left to itself the compiler can turn the stage offset into an induction variable
+  // with a bias that costs a second add per operand read.)
+  struct Bases {
+    int a[2], b[2], sa, sb;
+  };
+  auto bases = [&](int s) {
+    int so = (s % NB) * kStage;
+    asm volatile("" : "+s"(so));
+    Bases Bs;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      Bs.a[i] = a_base[i] + so;
+      Bs.b[i] = b_base[i] + so;
+    }
+    Bs.sa = sa_off + so;
+    Bs.sb = sb_off + so;
+    return Bs;
+  };
   // operands of 32-row tile pair i (A, B, s_x, s_w of tiles i) of group gg
-  auto read_half = [&](const uint8_t* st, int gg, int i, Frag& F) {
+  auto read_half = [&](const Bases& Bs, int gg, int i, Frag& F) {
     {
-      const v2u* pa = reinterpret_cast<const v2u*>(st + a_base[i] + gg * kFrag);
-      const v2u* pb = reinterpret_cast<const v2u*>(st + b_base[i] + gg * kFrag);
+      const v2u* pa = reinterpret_cast<const v2u*>(lds + Bs.a[i] + gg * kFrag);
+      const v2u* pb = reinterpret_cast<const v2u*>(lds + Bs.b[i] + gg * kFrag);
       const v2u a0 = pa[0], a1 = pa[1], a2 = pa[2];
       const v2u b0 = pb[0], b1 = pb[1], b2 = pb[2];
       F.A[i] = v8i{(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
       F.B[i] = v8i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y, (int)b2.x, (int)b2.y, 0, 0};
       if constexpr (!PARTIALS) {
-        const uint32_t sx = *reinterpret_cast<const uint32_t*>(st + sa_off + (64 * i + gg) * 4);
-        const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + sb_off + (gg * TN + 32 * i) * 4);
+        const uint32_t sx = *reinterpret_cast<const uint32_t*>(lds + Bs.sa + (64 * i + gg) * 4);
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(lds + Bs.sb + (gg * TN + 32 * i) * 4);
         F.SA[i] = __builtin_bit_cast(v4h, v2u{sx & sb_keep, 0u});
         F.SB[i] = __builtin_bit_cast(v4h, v2u{sw & sb_keep, 0u});
       }
     }
   };
-  auto read_frag = [&](const uint8_t* st, int gg, Frag& F) {
-    read_half(st, gg, 0, F);
-    read_half(st, gg, 1, F);
+  auto read_frag = [&](const Bases& Bs, int gg, Frag& F) {
+    read_half(Bs, gg, 0, F);
+    read_half(Bs, gg, 1, F);
   };
   auto fma8 = [](v16f& a, const v16f& p, const v16f& sp, int half) {
 #pragma unroll
@@ -316,11 +335,11 @@ void w4a4_gemm_e3m2_kernel(
     for (int s = 0; s < S; ++s) {
       wait_stage(s);
       if (s + 2 < S) issue_stage(s + 2);
-      const uint8_t* st = lds + (s % NB) * kStage;
+      const Bases Bs = bases(s);
       const int ng = min(KS, G - s * KS);
       for (int gg = 0; gg < ng; ++gg) {
         Frag F;
-        read_frag(st, gg, F);
+        read_frag(Bs, gg, F);
         const int g = s * KS + gg;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -353,10 +372,10 @@ void w4a4_gemm_e3m2_kernel(
                                (s + 2) * KS, s_gq, TM, TN);
       wait_stage(s);
       if (s == max(S - 2, 0)) issue_prefetch();
-      const uint8_t* st = lds + (s % NB) * kStage;
+      const Bases Bs = bases(s);
       const int ng = min(KS, G - s * KS);
       Frag F[KS];
-      read_frag(st, 0, F[0]);
+      read_frag(Bs, 0, F[0]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[1][1][e] = __builtin_fmaf(pp[e], spp[e ^ 1], acc[1][1][e]);
       asm volatile("" : "+v"(acc[1][1]));
@@ -372,7 +391,7 @@ void w4a4_gemm_e3m2_kernel(
           __builtin_amdgcn_sched_barrier(0);
           if (ISSUE && li < kLoads) issue_load(s + 2, R2, li);
           // (also in a last stage without a second group: its LDS holds a valid duplicate)
-          if (t < 2 && gg + 1 < KS) read_half(st, gg + 1, t, F[gg + 1]);
+          if (t < 2 && gg + 1 < KS) read_half(Bs, gg + 1, t, F[gg + 1]);
           // the pending tile: (1, 1) of the previous group at t == 0, else tile t - 1
           const int pi = t == 0 ? 1 : (t - 1) >> 1, pj = t == 0 ? 1 : (t - 1) & 1;
           const bool have = t > 0 || gg > 0;
