@@ -24,13 +24,15 @@
 //    while stage s is computed.  (The epilogue's T, L2 and bias, loaded once per tile, use
 //    global_load_lds.)  The tiled container's blocks are copied as they
 //    are, so an MFMA operand is three ds_read_b64 per lane from its 24-byte slot.
-//  * Scale products.  s_x[m] * s_w[n] for a 32 x 32 tile is an outer product that
-//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32) from one fp16 per
-//    lane read straight from LDS, with every k-slot but one zero (see the operand note in the
-//    kernel).  The dequantization is one FMA per output and group.
-//  * Epilogue.  bf16(T) [32 x 16] and L2 [16 x 32] fragments go through
-//    v_mfma_f32_32x32x16_bf16 with the fp32 accumulator as C, then the bias is added and the
-//    tile is rounded to bf16 (or kept fp32) and stored.
+//  * Scale products.  2 s_x[m] s_w[n] for a 32 x 32 tile is an outer product that
+//    v_mfma_f32_32x32x8_f16 computes exactly (fp16 x fp16 is exact in fp32, and it is the sum
+//    of two equal products) from one fp16 per lane read straight from LDS (see the operand note
+//    in the kernel).  The dequantization is one FMA per output and group, so the accumulator
+//    holds twice the dequantized sum -- exactly, as doubling commutes with rounding.
+//  * Epilogue.  bf16(2T) [32 x 16] and L2 [16 x 32] fragments go through
+//    v_mfma_f32_32x32x16_bf16 with the fp32 accumulator as C (bf16(2T) = 2 bf16(T) exactly),
+//    then Y = fma(acc, 1/2, bias) is rounded to bf16 (or kept fp32) and stored: the same
+//    values as without the factor 2.
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
@@ -129,7 +131,24 @@ void w4a4_gemm_e3m2_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to SGPRs
   const int wm = wave >> 1, wn = wave & 1;
-  const int m_tile = blockIdx.y * TM, n_tile = blockIdx.x * TN;
+  // XCD-aware tile order.  Workgroups go to the 8 XCDs round-robin by linear id, and each XCD
+  // has its own L2: linear id L runs on XCD L % 8 as that XCD's (L / 8)-th workgroup, so it
+  // takes logical tile (L % 8) T / 8 + L / 8 (a bijection on the first 8 floor(T / 8) ids;
+  // the rest keep their id), and each XCD walks a contiguous run of logical tiles.  Logical
+  // tiles go in bands of kBand row tiles, row tile fastest: the workgroups an XCD runs at once
+  // share kBand activation panels and a few weight panels, which stay in its L2 while it
+  // sweeps the columns.
+  constexpr int kBand = 8;
+  int m_tile, n_tile;
+  {
+    const int nx = gridDim.x, T = nx * gridDim.y, T8 = T / 8 * 8;
+    int L = blockIdx.y * nx + blockIdx.x;
+    if (L < T8) L = (L % 8) * (T / 8) + L / 8;
+    const int band = L / (kBand * nx), first = band * kBand;
+    const int rows = min((int)gridDim.y - first, kBand), within = L - band * kBand * nx;
+    m_tile = (first + within % rows) * TM;
+    n_tile = (within / rows) * TN;
+  }
 
   // ---- direct-to-LDS staging.  The codes arrive in the tiled container, whose (row block,
   //      group) blocks are exactly the MFMA operand blocks, so a stage is a copy of
@@ -216,15 +235,16 @@ void w4a4_gemm_e3m2_kernel(
   }
   // scale-product operands (v_mfma_f32_32x32x8_f16): lane l supplies k-slots 4 (l / 32) .. +3
   // of row (column) l % 32.  A is (s_x[row], 0, 0, 0) -- the zero-extended dword of s_x and a
-  // zero dword -- and B is (s_w[col], 0, 0, 0), both in lanes 0..31 only (zeros in lanes
-  // 32..63), so only k-slot 0 contributes and the MFMA returns s_x[row] * s_w[col] exactly.
+  // zero dword -- and B is (s_w[col], 0, 0, 0), in all 64 lanes, so k-slots 0 and 4 carry the
+  // same exact product and the MFMA returns 2 s_x[row] s_w[col] exactly.  (Zeroing lanes
+  // 32..63 instead, for s_x s_w itself, cost 8 VALU per stage in this VALU-bound loop; the
+  // factor 2 is taken out exactly at the store.)
   // Rows are read pairwise swapped ((l % 32) ^ 1): element e of the scale product then belongs
   // to element e ^ 1 of the partial, so the dequantization FMA acc[e] += p[e] * s[e ^ 1] reads
   // its three operands from different VGPR banks (acc, p and s are 16-register tiles whose
   // element e would otherwise share bank e % 4, which stalls the FMA).
   const int sa_off = 2 * (32 * 2 * wm + ((lane & 31) ^ 1)) * 4;  // + (64 i + gg) * 4
   const int sb_off = kScA + (32 * 2 * wn + (lane & 31)) * 4;    // + (gg * TN + 32 j) * 4
-  const uint32_t sb_keep = lane < 32 ? 0xFFFFFFFFu : 0u;
 
   v16f acc[2][2];
 #pragma unroll
@@ -302,8 +322,8 @@ void w4a4_gemm_e3m2_kernel(
       if constexpr (!PARTIALS) {
         const uint32_t sx = *reinterpret_cast<const uint32_t*>(lds + Bs.sa + (64 * i + gg) * 4);
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(lds + Bs.sb + (gg * TN + 32 * i) * 4);
-        F.SA[i] = __builtin_bit_cast(v4h, v2u{sx & sb_keep, 0u});
-        F.SB[i] = __builtin_bit_cast(v4h, v2u{sw & sb_keep, 0u});
+        F.SA[i] = __builtin_bit_cast(v4h, v2u{sx, 0u});
+        F.SB[i] = __builtin_bit_cast(v4h, v2u{sw, 0u});
       }
     }
   };
@@ -451,7 +471,8 @@ void w4a4_gemm_e3m2_kernel(
         const int x = wm * 64 + 32 * i + l32;
         const v4f t0 = *reinterpret_cast<const v4f*>(pb + ((k8 / 4) * TM + x) * 16);
         const v4f t1 = *reinterpret_cast<const v4f*>(pb + ((k8 / 4 + 1) * TM + x) * 16);
-        const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        const float tv[8] = {2.0f * t0.x, 2.0f * t0.y, 2.0f * t0.z, 2.0f * t0.w,
+                             2.0f * t1.x, 2.0f * t1.y, 2.0f * t1.z, 2.0f * t1.w};  // exact
         At[i] = to_bf16x8(tv);
       }
 #pragma unroll
@@ -472,7 +493,8 @@ void w4a4_gemm_e3m2_kernel(
       for (int i = 0; i < 2; ++i) {
         const v4f* tp = reinterpret_cast<const v4f*>(T + (size_t)min(row0 + 32 * i + l32, Mo - 1) * r + k8);
         const v4f t0 = tp[0], t1 = tp[1];
-        const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        const float tv[8] = {2.0f * t0.x, 2.0f * t0.y, 2.0f * t0.z, 2.0f * t0.w,
+                             2.0f * t1.x, 2.0f * t1.y, 2.0f * t1.z, 2.0f * t1.w};  // exact
         At[i] = to_bf16x8(tv);
       }
 #pragma unroll
@@ -507,7 +529,8 @@ void w4a4_gemm_e3m2_kernel(
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {  // rows e and e + 1 are consecutive (e % 4 in {0, 2})
           const uint32_t o = lo + (uint32_t)(32 * i + 8 * (e >> 2) + (e & 3)) * (uint32_t)N + 32 * j;
-          const float v0 = acc[i][j][e] + bj[j], v1 = acc[i][j][e + 1] + bj[j];
+          const float v0 = __builtin_fmaf(acc[i][j][e], 0.5f, bj[j]);
+          const float v1 = __builtin_fmaf(acc[i][j][e + 1], 0.5f, bj[j]);
           if constexpr (OUT_FP32) {
             float* y = reinterpret_cast<float*>(Y) + base;
             __builtin_nontemporal_store(v0, y + o);
@@ -530,7 +553,7 @@ void w4a4_gemm_e3m2_kernel(
       for (int e = 0; e < 16; ++e) {
         const int row = row0 + 32 * i + 8 * (e >> 2) + 4 * hi + (e & 3);
         if (row < Mo && col < No) {
-          const float v = acc[i][j][e] + bj[j];
+          const float v = __builtin_fmaf(acc[i][j][e], 0.5f, bj[j]);
           if constexpr (OUT_FP32)
             reinterpret_cast<float*>(Y)[(size_t)row * No + col] = v;
           else
