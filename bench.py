@@ -76,18 +76,26 @@ def parse():
 
 # HBM traffic of the GEMM kernel per launch, measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE, each scaled by what the same counter reads for a plain copy of known size).  The
-# measurement is recorded with the SHA-256 of the kernel source it was taken on; a different
-# source reports no traffic.
+# measurement is recorded with the SHA-256 of the kernel's sources (the kernel file, then the
+# device header it includes) it was taken on; different sources report no traffic.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "w4a4_gemm_e3m2_ffn_up_4608x3072x12288_traffic.md")
-GEMM_SOURCE = os.path.join(ROOT, "bit_post_quantized_amd", "csrc", "w4a4_gemm_e3m2.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "bit_post_quantized_amd", "csrc", f)
+                for f in ("w4a4_gemm_e3m2.hip", "svdq_device.hpp")]
+
+
+def gemm_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def recorded_traffic():
-    import hashlib
     try:
         rec = dict(line.split(":", 1) for line in open(TRAFFIC_RECORD).read().splitlines()
                    if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
-        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        src = gemm_source_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256", "").strip() != src:

@@ -185,4 +185,21 @@ __device__ __forceinline__ v4i unpack16_x16(v2u v) {
              (int)((v.y << 4) & 0xF0F0F0F0u), (int)(v.y & 0xF0F0F0F0u)};
 }
 
+// XCD-aware tile order for a GEMM grid of (column tiles, row tiles).  Workgroups go to the 8
+// XCDs round-robin by linear id, and each XCD has its own L2: linear id L runs on XCD L % 8 as
+// that XCD's (L / 8)-th workgroup, so it takes logical tile (L % 8) T / 8 + L / 8 (a bijection
+// on the first 8 floor(T / 8) ids; the rest keep their id) and each XCD walks a contiguous run
+// of logical tiles.  Logical tiles go in bands of `band` row tiles, row tile fastest: the
+// workgroups an XCD runs at once share `band` activation panels and a few weight panels, which
+// stay in its L2 while it sweeps the columns.  Returns (row tile, column tile).
+__device__ __forceinline__ void xcd_tile_order(int band, int& mt, int& nt) {
+  const int nx = gridDim.x, ny = gridDim.y, T = nx * ny, T8 = T / 8 * 8;
+  int L = blockIdx.y * nx + blockIdx.x;
+  if (L < T8) L = (L % 8) * (T / 8) + L / 8;
+  const int b = L / (band * nx), first = b * band;
+  const int rows = min(ny - first, band), within = L - b * band * nx;
+  mt = first + within % rows;
+  nt = within / rows;
+}
+
 }  // namespace svdq

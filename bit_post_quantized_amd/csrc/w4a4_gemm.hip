@@ -75,7 +75,10 @@ void w4a4_gemm_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / TL::WAVES_N, wn = wave % TL::WAVES_N;
   const int rl = lane & 15, kc = lane >> 4;
-  const int m_tile = blockIdx.y * TM, n_tile = blockIdx.x * TN;
+  int m_tile, n_tile;  // XCD-aware order, bands of 8 row tiles
+  xcd_tile_order(8, m_tile, n_tile);
+  m_tile *= TM;
+  n_tile *= TN;
   const int G = K / kGroup;
   const size_t ldq = (size_t)(K / 2);
 
