@@ -25,8 +25,8 @@ Before the step's warm-up, on the same process and device (outside the step), un
     and GEMM (random residual weights: the kernels' work does not depend on the values);
   * measured peaks of this device (FP6 / INT8 / bf16 MFMA issue loops and an HBM copy stream,
     libsvdq_peaks.so), against which each kernel's rate is also reported.
-These seconds of load also let the device's power management settle before the step is timed:
-from idle, the GEMM's first ~80 launches run 10-25 % slower than its steady state.
+These seconds of load also let the device settle before the step is timed: from idle, the
+GEMM's first ~80 launches run 10-25 % slower than its steady state.
 After the timed region: the oracle's stages on the host cores (cpu_baseline), unless
 --no-cpu-baseline.
 
@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # 100 warm-up steps (≈ 37 ms of load): from idle the GEMM needs about 80 steps to reach its
-    # steady rate (a power-management transient); the timed steps then measure that rate
+    # steady rate (a warm-up transient of the device); the timed steps then measure that rate
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -366,10 +366,10 @@ def main():
     ab = algorithmic_bytes()
 
     # The extra measurements run before the step is warmed up and timed: on a device fresh
-    # from idle, power management takes the first ~30 ms of sustained load to settle (the
-    # GEMM's first ~80 launches measured 216 -> 248 -> 194 us before holding at 194 us), and
-    # these measurements are several seconds of such load.  Their percentages of the measured
-    # peaks are computed once the step is timed.
+    # from idle the GEMM's first ~80 launches (~30 ms of load) ran 216 -> 248 -> 194 us before
+    # holding at 194 us (a transient whose shape is that of power management), and these
+    # measurements are several seconds of load.  Their percentages of the measured peaks are
+    # computed once the step is timed.
     def time10(fn, reps=10):
         fn()
         torch.cuda.synchronize()
