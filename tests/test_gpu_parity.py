@@ -272,9 +272,11 @@ def _gpu_kv(x_bits):
 # tokens (three passes) fill 200 chunks; (1, 2, 8) is a single token of 16 channels; (5, 2, 128)
 # is a single pass in which some token parts are empty; 2097120 tokens is the most one call
 # takes (65535 dequantization blocks of 32 tokens; three passes over 32768 range chunks)
+# (1001, 32, 128) and (37, 64, 128): the cache's row width and twice it, with a partial last
+# block of the dequantization (32 tokens)
 @pytest.mark.parametrize("shape", [(None, None, None), (1, 2, 8), (100, 4, 24), (1000, 8, 64),
                                    (2000, 16, 128), (5, 2, 128), (300, 3, 128), (12800, 32, 128),
-                                   (2097120, 1, 8)])
+                                   (2097120, 1, 8), (1001, 32, 128), (37, 64, 128)])
 def test_kv_quant_dequant_bitexact(gpu_lib, shape):
     for name, (x, ref) in kv_case(*shape).items():
         q, s, z, xo = _gpu_kv(x)
