@@ -85,8 +85,8 @@ int svdq_pack_lowrank(const uint16_t* L1, int K, int r, uint16_t* L1p, void* str
 
 /*
  * svdq_pack_lowrank_up — relayout of the 16-bit branch's up-projection factor for the GEMM
- * epilogue (offline weight preparation, like svdq_pack_lowrank).  Values are copied, not
- * rounded.
+ * epilogue (offline weight preparation, like svdq_pack_lowrank; SVDQ "technical principles":
+ * the rank-r branch L1 L2 kept in 16 bits).  Values are copied, not rounded.
  *   L2    bf16 [r, N] (row-major: element (j, n) at L2[j * N + n])
  *   L2p   bf16 [N, r] (element (j, n) at L2p[n * r + j]: each column's r values contiguous)
  *   16 <= r <= 128, r % 16 == 0, 1 <= N <= 2^24.
