@@ -9,11 +9,12 @@
 // log2(e) a score is  sum_c q'[c] qk[t, c] - sum_c q'[c] zk[c]  (the second sum is one number
 // per head), in the log2 domain; and sum_t p_t V'[t, c] = sv[c] (sum_t p_t qv[t, c] - zv[c]
 // sum_t p_t), so the value loop accumulates raw codes.  Split over tokens (flash-decoding):
-//  1. kv_attn_partial_kernel: one workgroup per (256-token chunk, head, query).  A thread owns
-//     16 channels of (256 / threads per row) tokens; every K and V code row it needs is loaded
-//     up front (16 bytes per row, 128 contiguous bytes per token and head).  Scores are
-//     reduced over the row's lanes with shuffles, the chunk max and sum over the workgroup,
-//     and the code-space output over tokens in LDS.  It writes (max, sum, O[D]) per chunk.
+//  1. kv_attn_partial_kernel: one workgroup per (head, 256-token chunk, query), head fastest.
+//     A thread owns 16 channels of (256 / threads per row) tokens; every K and V code row it
+//     needs is loaded up front (16 bytes per row, 128 contiguous bytes per token and head).
+//     Scores are reduced over the row's lanes with shuffles, the chunk max and sum over the
+//     workgroup, and the code-space output over tokens in LDS.  It writes (max, sum, O[D]) per
+//     chunk.  (Head fastest: 22.3 -> 21.6 us over the 10240-token, 32-head cache.)
 //  2. kv_attn_combine_kernel: per (head, query), rescales and sums the chunks' partials and
 //     applies sv, zv; writes bf16.  At most 4096 chunks (1M tokens) per call.
 #include "svdq_device.hpp"
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kAttnThreads) void kv_attn_partial_kernel(
   constexpr int PASSES = kAttnChunk / ROWS;   // token rows per thread
   __shared__ float red[ROWS][D + 4];
   __shared__ float wmax[kAttnThreads / 64], wsum[kAttnThreads / 64];
-  const int chunk = blockIdx.x, h = blockIdx.y, qi = blockIdx.z;
+  const int h = blockIdx.x, chunk = blockIdx.y, qi = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lc = tid % TPR, rr = tid / TPR;
   const int C = heads * D, c0 = h * D + lc * 16;
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kAttnThreads) void kv_attn_partial_kernel(
 #pragma unroll
   for (int j = 0; j < 16; ++j) red[rr][lc * 16 + j] = o16[j];
   __syncthreads();
-  float* out = ws + (((size_t)qi * heads + h) * gridDim.x + chunk) * (D + 2);
+  float* out = ws + (((size_t)qi * heads + h) * gridDim.y + chunk) * (D + 2);  // gridDim.y: chunks
   if (tid < D) {
     float acc = 0.0f;
 #pragma unroll 8
@@ -206,7 +207,9 @@ hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kq, const float
   const int nchunks = attn_chunks(tokens);
   float* ws = reinterpret_cast<float*>(workspace);
   const float qscale = sm_scale * 1.4426950408889634f;  // log2(e): the weights use exp2
-  const dim3 grid(nchunks, heads, nq);
+  // heads fastest: the workgroups of one chunk, one per head, are dispatched together and read
+  // whole 4 KB code rows between them instead of 128-byte slices of rows far apart in time
+  const dim3 grid(heads, nchunks, nq);
   if (dim == 128) {
     hipLaunchKernelGGL(kv_attn_partial_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, kq,
                        ks, kz, vq, tokens, heads, qscale, ws);
