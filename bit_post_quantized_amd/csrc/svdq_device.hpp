@@ -191,7 +191,8 @@ __device__ __forceinline__ v4i unpack16_x16(v2u v) {
 // on the first 8 floor(T / 8) ids; the rest keep their id) and each XCD walks a contiguous run
 // of logical tiles.  Logical tiles go in bands of `band` row tiles, row tile fastest: the
 // workgroups an XCD runs at once share `band` activation panels and a few weight panels, which
-// stay in its L2 while it sweeps the columns.  Returns (row tile, column tile).
+// stay in its L2 while it sweeps the columns.  Returns (row tile, column tile).  The int
+// arithmetic holds: the GEMMs' 128 x 128 tiles and M N <= 2^40 keep T below 2^27.
 __device__ __forceinline__ void xcd_tile_order(int band, int& mt, int& nt) {
   const int nx = gridDim.x, ny = gridDim.y, T = nx * ny, T8 = T / 8 * 8;
   int L = blockIdx.y * nx + blockIdx.x;
