@@ -23,6 +23,7 @@ Before the step's warm-up, on the same process and device (outside the step), un
     over the INT8 cache;
   * the attention (3072 x 3072) and FFN down-projection (12288 -> 3072) shapes' activation pass
     and GEMM (random residual weights: the kernels' work does not depend on the values);
+  * the step's GEMM alone, 100 launches back to back (last, just before the warm-up);
   * measured peaks of this device (FP6 / INT8 / bf16 MFMA issue loops and an HBM copy stream,
     libsvdq_peaks.so), against which each kernel's rate is also reported.
 These seconds of load also let the device settle before the step is timed: from idle, the
@@ -498,6 +499,16 @@ def main():
                            "weights": "random residual codes and factors (timing only)"}
             del Xs, wq6, ws6, L1p, L2s, inv, a_s, Ys
         extras["other_shapes"] = shapes
+        # ---- the step's GEMM alone (100 launches on one batch's codes), against its time inside
+        #      the step; measured last, so the device enters the step's warm-up settled on this
+        #      very load
+        a0 = acts[0]
+        B.svdq_quantize_act_e3m2(X[0], pw.inv_lambda, pw.L1p, RANK, a0.xq, a0.x_scales, a0.T, stream)
+        alone_ms = time10(lambda: B.svdq_w4a4_gemm_e3m2(a0.xq, a0.x_scales, a0.T, pw.wq, pw.w_scales,
+                                                        pw.L2p, None, RANK, Y[0], stream), reps=100)
+        extras["gemm_alone"] = {"ms": round(alone_ms, 5), "TOPS": round(tops(alone_ms), 2),
+                                "note": "svdq_w4a4_gemm_e3m2 at the step's shape, 100 launches "
+                                        "back to back on one batch (outside the step)"}
 
     names = ["act", "gemm", "kv_pair", "kv_dequant"]
     per_step = len(step_calls(0))
