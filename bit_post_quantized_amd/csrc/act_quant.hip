@@ -74,7 +74,7 @@ template <int NTR, int CODES, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r
 __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
-    uint16_t* __restrict__ x_scales, float* __restrict__ T) {
+    uint16_t* __restrict__ x_scales, float* __restrict__ T, int ksplit) {
   extern __shared__ float smem[];  // [K] inv_lambda (when staged), then [nwaves][16][r]
   constexpr int r = 16 * NTR;
   constexpr int NT = NTR > 0 ? NTR : 1;
@@ -85,7 +85,14 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   const int q = lane & 3;    // and quarter of the group
   const int src_byte = 4 * (4 * (lane & 15) + (lane >> 4));  // the MFMA layout's source lane
   const int G = K / kGroup;
-  const int row0 = blockIdx.x * kActRows;
+  // K split (long K): two neighbouring workgroups take the two halves of a row block's groups;
+  // their partial T meet by two atomic additions onto a zeroed T (exact for the first, and the
+  // same for either order: fl32(a + b) = fl32(b + a)), so the result is deterministic
+  const int half = ksplit ? (int)(blockIdx.x & 1) : 0;
+  const int Gh = (G + 1) / 2;
+  const int g_lo = ksplit ? half * Gh : 0;
+  const int g_hi = ksplit ? min(G, g_lo + Gh) : G;
+  const int row0 = (ksplit ? (int)(blockIdx.x >> 1) : (int)blockIdx.x) * kActRows;
   const int row = row0 + rl;
   const int row_ld = row < M ? row : M - 1;
   const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   v4u raw[kActBatch][2];
 #pragma unroll
   for (int b = 0; b < kActBatch; ++b) {
-    const int g = min(wave + b * nwaves, G - 1);
+    const int g = min(g_lo + wave + b * nwaves, g_hi - 1);
     const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
     raw[b][0] = p[0];
     raw[b][1] = p[1];
@@ -136,15 +143,15 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   // L1 operands, one group ahead of their use along the wave's whole sequence of groups (the
   // next batch's first group is requested under this batch's last)
   v4u bfr[2][NT][2];
-  load_l1(min(wave, G - 1), bfr[0]);
-  for (int j0 = wave; j0 < G; j0 += kActBatch * nwaves) {
-    const bool more = j0 + kActBatch * nwaves < G;  // uniform: this wave has a next batch
+  load_l1(min(g_lo + wave, g_hi - 1), bfr[0]);
+  for (int j0 = g_lo + wave; j0 < g_hi; j0 += kActBatch * nwaves) {
+    const bool more = j0 + kActBatch * nwaves < g_hi;  // uniform: this wave has a next batch
 #pragma unroll
     for (int b = 0; b < kActBatch; ++b) {
       const int g_raw = j0 + b * nwaves;
-      const bool gv = g_raw < G;  // uniform over the wave
-      const int g = gv ? g_raw : G - 1;
-      if (b + 1 < kActBatch || more) load_l1(min(j0 + (b + 1) * nwaves, G - 1), bfr[(b + 1) & 1]);
+      const bool gv = g_raw < g_hi;  // uniform over the wave
+      const int g = gv ? g_raw : g_hi - 1;
+      if (b + 1 < kActBatch || more) load_l1(min(j0 + (b + 1) * nwaves, g_hi - 1), bfr[(b + 1) & 1]);
       const int k0 = g * kGroup + 16 * q;
       v4f l0, l1, l2, l3;
       if constexpr (LAM_LDS) {
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
         xh[15] = __uint_as_float(w1.w & 0xFFFF0000u) * l3.w;
       }
       if (more) {  // refill slot b with group b of the next batch
-        const int gn = min(j0 + (kActBatch + b) * nwaves, G - 1);
+        const int gn = min(j0 + (kActBatch + b) * nwaves, g_hi - 1);
         const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)gn * kGroup);
         raw[b][0] = p[0];
         raw[b][1] = p[1];
@@ -282,7 +289,13 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
       const int rr = idx / r;
       float sum = 0.0f;
       for (int w = 0; w < nwaves; ++w) sum += red[(size_t)w * 16 * r + idx];
-      if (row0 + rr < M) T[(size_t)(row0 + rr) * r + (idx % r)] = sum;
+      if (row0 + rr < M) {
+        float* t = T + (size_t)(row0 + rr) * r + (idx % r);
+        if (ksplit)
+          atomicAdd(t, sum);
+        else
+          *t = sum;
+      }
     }
   }
 }
@@ -290,10 +303,10 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
 template <int CODES, bool LAM_LDS>
 static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                              int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                             int nwaves, size_t lds, hipStream_t stream) {
+                             int nwaves, size_t lds, int ksplit, hipStream_t stream) {
   // the tiled BF6 container is written up to the next multiple of 32 rows
   const int rows = CODES == kCodesBf6 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
-  const dim3 grid((rows + kActRows - 1) / kActRows), block(64 * nwaves);
+  const dim3 grid(((rows + kActRows - 1) / kActRows) << ksplit), block(64 * nwaves);
   switch (r / 16) {
 #define SVDQ_ACT_CASE(n)                                                                   \
   case n: {                                                                                \
@@ -303,7 +316,7 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
       if (e != hipSuccess) return e;                                                       \
     }                                                                                      \
     hipLaunchKernelGGL((quantize_act_kernel<n, CODES, LAM_LDS>), grid, block, lds, stream, X, \
-                       inv_lambda, L1, M, K, xq, x_scales, T);                             \
+                       inv_lambda, L1, M, K, xq, x_scales, T, ksplit);                     \
     break;                                                                                 \
   }
     SVDQ_ACT_CASE(0)
@@ -322,18 +335,43 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
   return hipGetLastError();
 }
 
+// zeroes T ahead of a K-split pass (a fill kernel, not a memset, so that the call can be
+// captured in a graph)
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0.0f;
+}
+
+// Groups per row block from which the pass splits K over two workgroups: with long K a row
+// block's workgroup runs long enough that the row blocks past one per CU (288 on 256 CUs at
+// 4608 tokens) double their CUs' time; halves balance that (FFN down, K = 12288: 4096 tokens
+// took 46.9 us, 4608 tokens 75 us).
+constexpr int kActSplitGroups = 96;
+
 template <int CODES>
 static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                    int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                                    hipStream_t stream) {
   const int G = K / kGroup;
+  const int ksplit = G >= kActSplitGroups ? 1 : 0;
+  const int Gw = ksplit ? (G + 1) / 2 : G;  // groups per workgroup
   const int maxw = act_max_waves(r / 16);
-  const int nwaves = G < maxw ? G : maxw;
+  const int nwaves = Gw < maxw ? Gw : maxw;
+  if (ksplit && r > 0 && M > 0) {
+    const size_t n = (size_t)M * r;
+    const size_t want = (n + 255) / 256;
+    const int blocks = want < 4096 ? (int)want : 4096;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, T, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const size_t red = (size_t)nwaves * 16 * r * sizeof(float);
   const size_t lam = (size_t)K * sizeof(float);
   if (lam + red <= kActLdsLambda)
-    return launch_act<CODES, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red, stream);
-  return launch_act<CODES, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, stream);
+    return launch_act<CODES, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red,
+                                   ksplit, stream);
+  return launch_act<CODES, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, ksplit,
+                                  stream);
 }
 
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,

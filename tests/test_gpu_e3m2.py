@@ -240,7 +240,9 @@ def test_e3m2_clamped_codes_of_subnormal_scales(gpu_lib):
 @pytest.mark.parametrize("M,K,N,r", [(1, 64, 24, 16), (17, 192, 136, 32), (129, 320, 129, 48),
                                      (7, 128, 1, 0), (300, 576, 260, 128),
                                      # more ragged tiles at G = 6, 10 and 24 groups
-                                     (130, 384, 260, 32), (45, 640, 72, 16), (257, 1536, 129, 0)])
+                                     (130, 384, 260, 32), (45, 640, 72, 16), (257, 1536, 129, 0),
+                                     # G = 96 and 97: the activation pass splits K in two
+                                     (37, 6144, 72, 32), (65, 6208, 40, 16)])
 def test_e3m2_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     d = make_linear(3, M=M, K=K, N=N, with_bias=True)
     pw = osq.prepare_weights(d["X"], d["W"], 0.5, r)

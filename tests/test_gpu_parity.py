@@ -194,8 +194,11 @@ def test_exact_ties_round_half_to_even(gpu_lib):
     assert (nudge == 0).sum() > M * K // 4  # many exact ties were exercised
 
 
+# (37, 6144, 72, 32) and (65, 6208, 40, 16): K / 64 = 96 and 97, where the activation pass
+# splits each row block's groups over two workgroups (97: halves of 49 and 48 groups)
 @pytest.mark.parametrize("M,K,N,r", [(1, 64, 24, 16), (17, 192, 136, 32), (129, 320, 129, 48),
-                                     (7, 128, 1, 0), (300, 576, 260, 128)])
+                                     (7, 128, 1, 0), (300, 576, 260, 128),
+                                     (37, 6144, 72, 32), (65, 6208, 40, 16)])
 def test_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     d = make_linear(3, M=M, K=K, N=N, with_bias=True)
     pw = osq.prepare_weights(d["X"], d["W"], 0.5, r)
