@@ -242,7 +242,8 @@ def test_e3m2_clamped_codes_of_subnormal_scales(gpu_lib):
                                      # more ragged tiles at G = 6, 10 and 24 groups
                                      (130, 384, 260, 32), (45, 640, 72, 16), (257, 1536, 129, 0),
                                      # G = 96 and 97: the activation pass splits K in two
-                                     (37, 6144, 72, 32), (65, 6208, 40, 16)])
+                                     # (and at rank 0, with no T to combine)
+                                     (37, 6144, 72, 32), (65, 6208, 40, 16), (33, 6144, 40, 0)])
 def test_e3m2_ragged_shapes_with_guard_bands(gpu_lib, M, K, N, r):
     d = make_linear(3, M=M, K=K, N=N, with_bias=True)
     pw = osq.prepare_weights(d["X"], d["W"], 0.5, r)
