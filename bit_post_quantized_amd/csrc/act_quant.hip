@@ -7,8 +7,9 @@
 // token and 64-group; b = 4 (INT4 codes) or b = 8 (the W4A8 variant's activations, W4A8 1).
 // SVDQ / DCMP: the branch is fused so the activations are read from HBM once.
 //
-// Work decomposition.  A workgroup owns 16 tokens (rows) and all of K; its waves take the
-// 64-groups round-robin.  In a group, lane l holds row l / 4 and the 16 consecutive k
+// Work decomposition.  A workgroup owns 16 tokens (rows) and all of K, or half of K (long K),
+// or, with long K and more row blocks than CUs, an equal share of the (row block, group) units
+// that may span three row blocks; its waves take the 64-groups round-robin.  In a group, lane l holds row l / 4 and the 16 consecutive k
 // [16 q, 16 q + 16) of quarter q = l % 4: two 16-byte loads, and the four lanes of a quad read
 // one row's 128 contiguous bytes.  (The vector memory unit resolves a 16-byte load four lanes
 // at a time; with the four lanes of a quad on four different rows, the same loads took twice
@@ -25,7 +26,11 @@
 // lane permutation (ds_bpermute: lane l takes lane 4 (l % 16) + l / 16) into the operand
 // layout of v_mfma_f32_16x16x32_bf16, row or column l % 16 and k-slots 8 (l / 16) + i; two
 // MFMAs per group take k = 16 q + i and 16 q + 8 + i, so they sum exactly the group's 64 k.
-// Per-wave partial T tiles are summed in LDS in wave order (deterministic) and written once.
+// Per-wave partial T tiles are summed in LDS in wave order (deterministic) and written once,
+// or, where two workgroups share a row block, added atomically onto a zeroed T (two additions:
+// deterministic, but at long K the rounding of T then depends on where the shares fall).
+#include <atomic>
+
 #include "svdq_device.hpp"
 #include "svdq_launch.hpp"
 
@@ -43,11 +48,16 @@ constexpr int kActRows = 16;    // tokens per workgroup
 // groups in flight and refills each slot with the next batch's group once it has been read:
 // 3 groups for the nibble and int8 containers, 2 for BF6 (whose conversion needs 16 more
 // registers).  Larger ranks (LoRA adapters) hold more low-rank operands and accumulators
-// (<= 256 VGPRs): batches of 6 groups, and from rank 96 on, batches of 3 (no spills at any
-// rank).
+// (<= 256 VGPRs): batches of 6 groups, from rank 96 on batches of 3, and from rank 112 on
+// batches of 2 (rank 128 still spills 4 to 25 dwords, by container).
 constexpr int act_max_waves(int) { return 8; }
+// Balanced grid (long K): when the row blocks outnumber the CUs but not twice over, one
+// workgroup of 16 waves per CU takes an equal share of the (row block, group) units (ranks up
+// to 32: at most 120 VGPRs, so 16 waves fit a CU).
+constexpr int kActWideWaves = 16;
+constexpr int kActShareSegs = 3;  // row blocks a share of at most 2 G units can span
 constexpr int act_batch(int ntr, int codes) {
-  return codes == kCodesBf6 && ntr <= 2 ? 2 : ntr <= 2 || ntr >= 6 ? 3 : 6;
+  return (codes == kCodesBf6 && ntr <= 2) || ntr >= 7 ? 2 : ntr <= 2 || ntr >= 6 ? 3 : 6;
 }
 constexpr size_t kActLdsLambda = 96 * 1024;  // inv_lambda staged in LDS while it fits
 
@@ -69,49 +79,80 @@ __device__ __forceinline__ v4u quad_to_mfma(v4u v, int src_byte) {
              (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.w)};
 }
 
+// A unit of work: row block rb (16 rows) x 64-group g, u = rb G + g.
+struct ActUnit {
+  int u, rb, g;
+};
+
 // CODES: kCodesNibbles, kCodesBf6 (INT4 codes) or kCodesInt8 (8-bit codes of the W4A8 variant)
-template <int NTR, int CODES, bool LAM_LDS>  // NTR: 16-wide tiles of the rank r (r = 16 * NTR)
-__global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
+// WAVES: the most waves a workgroup is launched with (the register budget follows from it);
+// kActWideWaves is the balanced grid, whose shares span several row blocks (SHARE), and 8 the
+// grid of one or two workgroups per row block
+template <int NTR, int CODES, bool LAM_LDS, int WAVES>  // NTR: 16-wide tiles of the rank r = 16 NTR
+__global__ __launch_bounds__(64 * WAVES) void quantize_act_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ inv_lambda,
     const uint16_t* __restrict__ L1, int M, int K, uint8_t* __restrict__ xq,
-    uint16_t* __restrict__ x_scales, float* __restrict__ T, int ksplit) {
-  extern __shared__ float smem[];  // [K] inv_lambda (when staged), then [nwaves][16][r]
+    uint16_t* __restrict__ x_scales, float* __restrict__ T, int nrb, int tadd) {
+  // [K] inv_lambda (when staged), then the partial T slots [segments][nwaves][16][r]
+  extern __shared__ float smem[];
   constexpr int r = 16 * NTR;
   constexpr int NT = NTR > 0 ? NTR : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int rl = lane >> 2;  // this lane's row of the block
   const int q = lane & 3;    // and quarter of the group
   const int src_byte = 4 * (4 * (lane & 15) + (lane >> 4));  // the MFMA layout's source lane
   const int G = K / kGroup;
-  // K split (long K): two neighbouring workgroups take the two halves of a row block's groups;
-  // their partial T meet by two atomic additions onto a zeroed T (exact for the first, and the
-  // same for either order: fl32(a + b) = fl32(b + a)), so the result is deterministic
-  const int half = ksplit ? (int)(blockIdx.x & 1) : 0;
-  const int Gh = (G + 1) / 2;
-  const int g_lo = ksplit ? half * Gh : 0;
-  const int g_hi = ksplit ? min(G, g_lo + Gh) : G;
-  const int row0 = (ksplit ? (int)(blockIdx.x >> 1) : (int)blockIdx.x) * kActRows;
-  const int row = row0 + rl;
-  const int row_ld = row < M ? row : M - 1;
-  const uint16_t* xrow = X + (size_t)row_ld * K + 16 * q;
+  constexpr bool SHARE = WAVES == kActWideWaves;
+  // The workgroup's share: units [u_lo, u_hi) of the nrb G units, split evenly over the grid.
+  // One workgroup per row block (u_lo = rb G), two per row block (its halves, long K), or an
+  // even share of at least G units per workgroup (more row blocks than CUs).  A share of at
+  // least G units meets a row block's G units in at most two shares, so a row block's T is
+  // either written by its one workgroup, or the sum of two partials added atomically onto a
+  // zeroed T (the first addition is exact and fl32(a + b) = fl32(b + a): deterministic).  A
+  // share of at most 2 G units spans at most three row blocks (kActShareSegs partial T slots).
+  const long long U = (long long)nrb * G;
+  const int u_lo = (int)((long long)blockIdx.x * U / gridDim.x);
+  const int u_hi = (int)((long long)(blockIdx.x + 1) * U / gridDim.x);
+  const int rb_first = u_lo / G;
+  const ActUnit last{u_hi - 1, (u_hi - 1) / G, (u_hi - 1) % G};
+  auto unit = [&](int u) { return ActUnit{u, u / G, u % G}; };
+  // the wave's units are u_lo + wave + k nwaves; a unit past the share is clamped to the last
+  // one (a clamped duplicate is computed but neither stored nor accumulated)
+  auto clamp_unit = [&](const ActUnit& p) { return p.u < u_hi ? p : last; };
+  // (one row block per share: the row block never changes, and a unit past it is clamped)
+  auto advance = [&](ActUnit& p) {
+    p.u += nwaves;
+    p.g += nwaves;
+    if constexpr (SHARE) {
+      while (p.g >= G) {
+        p.g -= G;
+        ++p.rb;
+      }
+    }
+  };
+  auto row_block = [&](const ActUnit& p) { return SHARE ? p.rb : rb_first; };
+  auto xptr = [&](const ActUnit& p) {
+    const int rw = min(row_block(p) * kActRows + rl, M - 1);
+    return reinterpret_cast<const v4u*>(X + (size_t)rw * K + (size_t)p.g * kGroup + 16 * q);
+  };
   float* lam = smem;
   float* red = smem + (LAM_LDS ? K : 0);
 
   constexpr int kActBatch = act_batch(NTR, CODES);
-  // Rolling pipeline over the wave's groups j0 + b nwaves: slot b of raw holds the activations
-  // of the batch's group b, and is refilled with group b of the next batch as soon as it has
-  // been read, so the next batch's loads are in flight under this batch's work (group index
-  // clamped; a clamped duplicate is computed but neither stored nor accumulated).  The first
-  // batch is requested before inv_lambda is staged, so the two round trips overlap.
+  // Rolling pipeline over the wave's units: slot b of raw holds the activations of the batch's
+  // unit b, and is refilled with unit b of the next batch as soon as it has been read, so the
+  // next batch's loads are in flight under this batch's work.  The first batch is requested
+  // before inv_lambda is staged, so the two round trips overlap.
   v4u raw[kActBatch][2];
+  ActUnit fill = unit(u_lo + wave);  // the unit whose activations are loaded next
 #pragma unroll
   for (int b = 0; b < kActBatch; ++b) {
-    const int g = min(g_lo + wave + b * nwaves, g_hi - 1);
-    const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)g * kGroup);
+    const v4u* p = xptr(clamp_unit(fill));
     raw[b][0] = p[0];
     raw[b][1] = p[1];
+    advance(fill);
   }
 
   // inv_lambda is shared by every row: one coalesced copy into LDS per workgroup, so the group
@@ -120,8 +161,12 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   if constexpr (LAM_LDS) {
     for (int i = threadIdx.x; i < K / 4; i += blockDim.x)
       reinterpret_cast<v4f*>(lam)[i] = reinterpret_cast<const v4f*>(inv_lambda)[i];
-    __syncthreads();
   }
+  // with several row blocks per share, a wave may meet only some of them: its other partial
+  // T slots stay zero
+  if constexpr (SHARE && NTR > 0)
+    for (int i = threadIdx.x; i < kActShareSegs * nwaves * 16 * r; i += blockDim.x) red[i] = 0.0f;
+  if constexpr (LAM_LDS || (SHARE && NTR > 0)) __syncthreads();
 
   v4f acc[NT];
 #pragma unroll
@@ -140,18 +185,35 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
     }
   };
 
-  // L1 operands, one group ahead of their use along the wave's whole sequence of groups (the
-  // next batch's first group is requested under this batch's last)
+  // this wave's partial T (acc) belongs to row block rb_acc; it moves to slot
+  // rb_acc - rb_first of the wave when the wave's units pass into the next row block
+  auto flush = [&](int rb) {
+    if constexpr (NTR > 0) {
+      // D layout of a 16x16 MFMA tile: lane l holds column l % 16 and rows 4 (l / 16) + i.
+      float* slot = red + ((size_t)(rb - rb_first) * nwaves + wave) * 16 * r;
+#pragma unroll
+      for (int t = 0; t < NTR; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot[(4 * (lane >> 4) + i) * r + t * 16 + (lane & 15)] = acc[t][i];
+    }
+  };
+
+  // L1 operands, one unit ahead of their use along the wave's whole sequence of units (the
+  // next batch's first unit is requested under this batch's last)
+  ActUnit cur = unit(u_lo + wave);  // the unit computed next
+  int rb_acc = row_block(clamp_unit(cur));
   v4u bfr[2][NT][2];
-  load_l1(min(g_lo + wave, g_hi - 1), bfr[0]);
-  for (int j0 = g_lo + wave; j0 < g_hi; j0 += kActBatch * nwaves) {
-    const bool more = j0 + kActBatch * nwaves < g_hi;  // uniform: this wave has a next batch
+  load_l1(clamp_unit(cur).g, bfr[0]);
+  for (int j0 = u_lo + wave; j0 < u_hi; j0 += kActBatch * nwaves) {
+    const bool more = j0 + kActBatch * nwaves < u_hi;  // uniform: this wave has a next batch
 #pragma unroll
     for (int b = 0; b < kActBatch; ++b) {
-      const int g_raw = j0 + b * nwaves;
-      const bool gv = g_raw < g_hi;  // uniform over the wave
-      const int g = gv ? g_raw : g_hi - 1;
-      if (b + 1 < kActBatch || more) load_l1(min(j0 + (b + 1) * nwaves, g_hi - 1), bfr[(b + 1) & 1]);
+      const bool gv = cur.u < u_hi;  // uniform over the wave
+      const ActUnit cu = clamp_unit(cur);
+      const int g = cu.g;
+      const int row = row_block(cu) * kActRows + rl;
+      advance(cur);
+      if (b + 1 < kActBatch || more) load_l1(clamp_unit(cur).g, bfr[(b + 1) & 1]);
       const int k0 = g * kGroup + 16 * q;
       v4f l0, l1, l2, l3;
       if constexpr (LAM_LDS) {
@@ -181,12 +243,12 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
         xh[14] = __uint_as_float(w1.w << 16) * l3.z;
         xh[15] = __uint_as_float(w1.w & 0xFFFF0000u) * l3.w;
       }
-      if (more) {  // refill slot b with group b of the next batch
-        const int gn = min(j0 + (kActBatch + b) * nwaves, g_hi - 1);
-        const v4u* p = reinterpret_cast<const v4u*>(xrow + (size_t)gn * kGroup);
+      if (more) {  // refill slot b with unit b of the next batch
+        const v4u* p = xptr(clamp_unit(fill));
         raw[b][0] = p[0];
         raw[b][1] = p[1];
       }
+      advance(fill);
 
       // ---- group max over the row's four quarter lanes, scale, codes
       float amax = 0.0f;
@@ -253,8 +315,16 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
         }
       }
 
-      // ---- low-rank down-projection on bf16 MFMA (a clamped duplicate group adds zero)
+      // ---- low-rank down-projection on bf16 MFMA (a clamped duplicate unit adds zero)
       if constexpr (NTR > 0) {
+        if constexpr (SHARE) {
+          if (gv && cu.rb != rb_acc) {  // uniform: the wave passes into the next row block
+            flush(rb_acc);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+            rb_acc = cu.rb;
+          }
+        }
         v8bf a0 = __builtin_bit_cast(v8bf, quad_to_mfma(__builtin_bit_cast(v4u, to_bf16x8(xh)), src_byte));
         v8bf a1 = __builtin_bit_cast(v8bf, quad_to_mfma(__builtin_bit_cast(v4u, to_bf16x8(xh + 8)), src_byte));
         if (!gv) a0 = a1 = v8bf{};
@@ -278,20 +348,19 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   }
 
   if constexpr (NTR > 0) {
-    // D layout of a 16x16 MFMA tile: lane l holds column l % 16 and rows 4 * (l / 16) + i.
-#pragma unroll
-    for (int t = 0; t < NTR; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        red[((size_t)wave * 16 + 4 * (lane >> 4) + i) * r + t * 16 + (lane & 15)] = acc[t][i];
+    flush(rb_acc);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * r; idx += blockDim.x) {
-      const int rr = idx / r;
+    // each row block's partial: the waves' partials summed in wave order
+    const int nused = last.rb - rb_first + 1;
+    for (int idx = threadIdx.x; idx < nused * 16 * r; idx += blockDim.x) {
+      const int sg = idx / (16 * r), within = idx - sg * 16 * r;
+      const float* slots = red + (size_t)sg * nwaves * 16 * r + within;
       float sum = 0.0f;
-      for (int w = 0; w < nwaves; ++w) sum += red[(size_t)w * 16 * r + idx];
-      if (row0 + rr < M) {
-        float* t = T + (size_t)(row0 + rr) * r + (idx % r);
-        if (ksplit)
+      for (int w = 0; w < nwaves; ++w) sum += slots[(size_t)w * 16 * r];
+      const int rw = (rb_first + sg) * kActRows + within / r;
+      if (rw < M) {
+        float* t = T + (size_t)rw * r + (within % r);
+        if (tadd)
           atomicAdd(t, sum);
         else
           *t = sum;
@@ -300,24 +369,27 @@ __global__ __launch_bounds__(64 * act_max_waves(NTR)) void quantize_act_kernel(
   }
 }
 
-template <int CODES, bool LAM_LDS>
+template <int CODES, bool LAM_LDS, int WAVES>
 static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                              int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
-                             int nwaves, size_t lds, int ksplit, hipStream_t stream) {
-  // the tiled BF6 container is written up to the next multiple of 32 rows
-  const int rows = CODES == kCodesBf6 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
-  const dim3 grid(((rows + kActRows - 1) / kActRows) << ksplit), block(64 * nwaves);
+                             int nrb, int grid, int nwaves, int tadd, size_t lds,
+                             hipStream_t stream) {
   switch (r / 16) {
-#define SVDQ_ACT_CASE(n)                                                                   \
-  case n: {                                                                                \
-    const void* fn = reinterpret_cast<const void*>(quantize_act_kernel<n, CODES, LAM_LDS>);  \
-    if (lds > 64 * 1024) {                                                                 \
-      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (e != hipSuccess) return e;                                                       \
-    }                                                                                      \
-    hipLaunchKernelGGL((quantize_act_kernel<n, CODES, LAM_LDS>), grid, block, lds, stream, X, \
-                       inv_lambda, L1, M, K, xq, x_scales, T, ksplit);                     \
-    break;                                                                                 \
+#define SVDQ_ACT_CASE(n)                                                                     \
+  case n: {                                                                                  \
+    if constexpr (WAVES <= act_max_waves(n) || n <= 2) { /* 16 waves: rank <= 32 */       \
+      const void* fn = reinterpret_cast<const void*>(quantize_act_kernel<n, CODES, LAM_LDS, WAVES>); \
+      if (lds > 64 * 1024) {                                                                 \
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+        if (e != hipSuccess) return e;                                                       \
+      }                                                                                      \
+      hipLaunchKernelGGL((quantize_act_kernel<n, CODES, LAM_LDS, WAVES>), dim3(grid),       \
+                         dim3(64 * nwaves), lds, stream, X, inv_lambda, L1, M, K, xq, x_scales, \
+                         T, nrb, tadd);                                                      \
+      break;                                                                                 \
+    } else {                                                                                 \
+      return hipErrorInvalidValue;                                                           \
+    }                                                                                        \
   }
     SVDQ_ACT_CASE(0)
     SVDQ_ACT_CASE(1)
@@ -335,43 +407,98 @@ static hipError_t launch_act(const uint16_t* X, const float* inv_lambda, const u
   return hipGetLastError();
 }
 
-// zeroes T ahead of a K-split pass (a fill kernel, not a memset, so that the call can be
-// captured in a graph)
+// zeroes T ahead of a pass whose row blocks are shared by two workgroups (a fill kernel, not
+// a memset, so that the call can be captured in a graph)
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
     p[i] = 0.0f;
 }
 
-// Groups per row block from which the pass splits K over two workgroups: with long K a row
-// block's workgroup runs long enough that the row blocks past one per CU (288 on 256 CUs at
-// 4608 tokens) double their CUs' time; halves balance that (FFN down, K = 12288: 4096 tokens
-// took 46.9 us, 4608 tokens 75 us).
+// Groups per row block from which the pass splits K: with long K a row block's workgroup runs
+// long enough that the row blocks past one per CU double their CUs' time.  Up to one row
+// block per CU each row block's halves go to two workgroups; with more (but fewer than two per
+// CU), the balanced grid gives every CU an equal share.  FFN down (K = 12288, rank 32): 4096
+// tokens took 46.9 us with one workgroup per row block; 4608 tokens 75 us, 64 us in halves,
+// 55.8 us on the balanced grid.  At shorter K the balanced grid lost (4608 x 3072: 18.4 ->
+// 22.0 us; the fill of T and the shares' partial sums cost more than the balance saves).
 constexpr int kActSplitGroups = 96;
+
+// the current device's CU count and largest LDS allocation per workgroup (0 if unknown)
+struct ActDevice {
+  int cus, lds;
+};
+static ActDevice act_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<long long> cache[kMaxDevices];  // cus << 32 | lds, + 1; 0 = not queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return {0, 0};
+  }
+  const long long c = cache[dev].load(std::memory_order_relaxed);
+  if (c) return {(int)((c - 1) >> 32), (int)((c - 1) & 0xFFFFFFFF)};
+  int cus = 0, lds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+    (void)hipGetLastError();  // leave no sticky error behind; use the per-row-block grid
+    return {0, 0};
+  }
+  cache[dev].store((((long long)cus << 32) | (unsigned)lds) + 1, std::memory_order_relaxed);
+  return {cus, lds};
+}
 
 template <int CODES>
 static hipError_t launch_act_route(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,
                                    int M, int K, int r, uint8_t* xq, uint16_t* x_scales, float* T,
                                    hipStream_t stream) {
   const int G = K / kGroup;
+  // the tiled BF6 container is written up to the next multiple of 32 rows
+  const int rows = CODES == kCodesBf6 ? (M + kE3m2Rows - 1) / kE3m2Rows * kE3m2Rows : M;
+  const int nrb = (rows + kActRows - 1) / kActRows;
+  const size_t lam = (size_t)K * sizeof(float);
+  // Balanced grid (long K, between one and two row blocks per CU, rank <= 32): one workgroup
+  // of 16 waves per CU, each with an even share of the units (at least G and at most 2 G).
+  const ActDevice dev = act_device();
+  static_assert(kActSplitGroups >= kActWideWaves, "a wave's next unit is at most one row block on");
+  if (r <= 32 && G >= kActSplitGroups && dev.cus > 0 && nrb > dev.cus && nrb < 2 * dev.cus) {
+    const size_t red = (size_t)kActShareSegs * kActWideWaves * 16 * r * sizeof(float);
+    if (red <= (size_t)dev.lds) {
+      if (r > 0) {
+        const size_t n = (size_t)M * r;
+        const size_t want = (n + 255) / 256;
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(want < 4096 ? (int)want : 4096), dim3(256), 0,
+                           stream, T, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if (lam + red <= (size_t)dev.lds)
+        return launch_act<CODES, true, kActWideWaves>(X, inv_lambda, L1, M, K, r, xq, x_scales, T,
+                                                      nrb, dev.cus, kActWideWaves, 1, lam + red,
+                                                      stream);
+      return launch_act<CODES, false, kActWideWaves>(X, inv_lambda, L1, M, K, r, xq, x_scales, T,
+                                                     nrb, dev.cus, kActWideWaves, 1, red, stream);
+    }
+  }
+  // one workgroup per row block, or two (its halves) from kActSplitGroups groups on
   const int ksplit = G >= kActSplitGroups ? 1 : 0;
   const int Gw = ksplit ? (G + 1) / 2 : G;  // groups per workgroup
   const int maxw = act_max_waves(r / 16);
   const int nwaves = Gw < maxw ? Gw : maxw;
-  if (ksplit && r > 0 && M > 0) {
+  if (ksplit && r > 0) {
     const size_t n = (size_t)M * r;
     const size_t want = (n + 255) / 256;
-    const int blocks = want < 4096 ? (int)want : 4096;
-    hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, T, n);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(want < 4096 ? (int)want : 4096), dim3(256), 0, stream,
+                       T, n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const size_t red = (size_t)nwaves * 16 * r * sizeof(float);
-  const size_t lam = (size_t)K * sizeof(float);
+  const int grid = nrb << ksplit;
   if (lam + red <= kActLdsLambda)
-    return launch_act<CODES, true>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, lam + red,
-                                   ksplit, stream);
-  return launch_act<CODES, false>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nwaves, red, ksplit,
-                                  stream);
+    return launch_act<CODES, true, 8>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nrb, grid,
+                                      nwaves, ksplit, lam + red, stream);
+  return launch_act<CODES, false, 8>(X, inv_lambda, L1, M, K, r, xq, x_scales, T, nrb, grid, nwaves,
+                                     ksplit, red, stream);
 }
 
 hipError_t launch_quantize_act(const uint16_t* X, const float* inv_lambda, const uint16_t* L1,

@@ -4,8 +4,8 @@ At 4608 rows the pass runs 288 workgroups of 16 rows, more than a 256-CU device 
 The last 512 rows quantized in a call of their own (32 workgroups) must give the same codes,
 scales and T, bit for bit: each row's outputs depend on that row alone, and T is summed in a
 fixed wave order.  This covers every code container and the launch configurations of the
-low-rank branch: none, rank 32 (16 waves), rank 48 (8 waves, batches of 6) and rank 112
-(8 waves, batches of 3).
+low-rank branch: none, rank 32 (batches of 2 groups in flight for BF6, 3 otherwise), rank 48
+(batches of 6) and rank 112 (batches of 2); 8 waves per workgroup in every case.
 """
 import numpy as np
 import pytest
