@@ -256,12 +256,12 @@ __global__ __launch_bounds__(64 * WAVES) void quantize_act_kernel(
       for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xh[i]));
       amax = max_row_quarters(amax);
       constexpr bool I8 = CODES == kCodesInt8;
-      const uint16_t sb = I8 ? float_to_half_bits(amax / 127.0f) : int4_scale_bits(amax);
+      const uint16_t sb = I8 ? int8_scale_bits(amax) : int4_scale_bits(amax);
       const float s = half_bits_to_float(sb);
       const float s1 = s == 0.0f ? 1.0f : s;  // an all-zero group: every quotient is 0
       const bool live = row < M;
       // padding rows get 1 / s = 0: every quotient is then exactly 0, so no select per code
-      const float rcp = live ? 1.0f / s1 : 0.0f;
+      const float rcp = live ? rcp_rn_half(s1) : 0.0f;
       // code + 8 (+ 128 for 8-bit codes) as bytes: rne of the correctly rounded quotient, the
       // bias, clamp to [0, 15] ([0, 255]); a -0 quotient becomes the bias, so both zeros give 0
       constexpr float kBias = I8 ? 128.0f : 8.0f, kTop = I8 ? 255.0f : 15.0f;

@@ -66,10 +66,35 @@ __device__ __forceinline__ float rne_quotient(float x, float s, float rcp) {
   return __builtin_rintf(div_rn(x, s, rcp));
 }
 
-// Symmetric INT4 scale of a group from its max magnitude: fp16(fl32(amax / 7)).
-__device__ __forceinline__ uint16_t int4_scale_bits(float amax) {
-  return float_to_half_bits(amax / 7.0f);
+// fl32(1 / s) for s an fp16 value held in fp32 (s != 0): the hardware reciprocal, which is within
+// one ulp, refined by one correction step y + y (1 - s y) in two FMAs.  For every fp16
+// significand and every start within two ulps of 1 / s this is the correctly rounded
+// reciprocal (an exact-rational enumeration of all 1024 significands); 1 / s of an fp16 is a
+// normal fp32, so the exponent only scales.
+__device__ __forceinline__ float rcp_rn_half(float s) {
+  const float y = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y, 1.0f);
+  return __builtin_fmaf(e, y, y);
 }
+
+// fp16(fl32(amax / d)) with the quotient by the correction step above and the correctly rounded
+// constant fl32(1 / d) (a quotient in fp32's subnormal range rounds to an fp16 zero either way).
+// The fp32 quotient is kept opaque before the conversion: left to itself the compiler fuses the
+// last FMA with the conversion (v_fma_mixlo_f16), which rounds once, straight to fp16, and
+// differs from the two roundings the scale is defined by.
+template <int D>
+__device__ __forceinline__ uint16_t scale_bits_div(float amax) {
+  constexpr float kRcp = 1.0f / (float)D;
+  float q = div_rn(amax, (float)D, kRcp);
+  asm volatile("" : "+v"(q));
+  return float_to_half_bits(q);
+}
+
+// Symmetric INT4 scale of a group from its max magnitude: fp16(fl32(amax / 7)).
+__device__ __forceinline__ uint16_t int4_scale_bits(float amax) { return scale_bits_div<7>(amax); }
+
+// The 8-bit variant's scale fp16(fl32(amax / 127)).
+__device__ __forceinline__ uint16_t int8_scale_bits(float amax) { return scale_bits_div<127>(amax); }
 
 // Eight codes (floats holding integers in [-8, 7]) -> one dword of nibbles, code i in bits
 // 4i .. 4i+3, two's complement: bias by 8, convert to bytes, merge even / odd, un-bias.
